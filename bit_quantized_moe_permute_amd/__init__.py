@@ -1,0 +1,160 @@
+"""Routed 2-bit MoE FFN layer for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/moe2bit.h (libmoe2bit.so, built
+in-tree by build.py).  The functions below have the C names and only marshal
+arguments: torch tensors are passed as device pointers, the stream is torch's
+current HIP stream, and every step of the layer runs in the library's HIP
+kernels.  There is no fallback: if the library is missing or fails to load,
+importing the binding raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe2bit.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE = 0, 1, 2, 3
+DT_F32, DT_BF16 = 0, 1
+FMT_IQ2X, FMT_Q2K, FMT_Q4K = 1, 2, 3
+PATH_AUTO, PATH_GENERIC, PATH_GEMV, PATH_GEMM = 0, 1, 2, 3
+ABI_VERSION = 1
+
+EXPORTS = [
+    "moe_abi_version", "moe_last_error", "moe_weight_bytes", "moe_prepare_weights", "moe_dequantize",
+    "moe_route_workspace", "moe_route", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_combine",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+class LayerDesc(ctypes.Structure):
+    """moe_layer_desc (include/moe2bit.h)."""
+    _fields_ = [
+        ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("gate_up_fmt", ctypes.c_int32), ("down_fmt", ctypes.c_int32),
+        ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
+        ("codebook", ctypes.c_void_p),
+        ("shared_inter", ctypes.c_int32),
+        ("shared_gate", ctypes.c_void_p), ("shared_up", ctypes.c_void_p), ("shared_down", ctypes.c_void_p),
+        ("path", ctypes.c_int32),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python bit_quantized_moe_permute_amd/build.py` "
+                          f"(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.moe_abi_version.restype = ctypes.c_int
+    L.moe_abi_version.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_weight_bytes.restype = sz
+    L.moe_weight_bytes.argtypes = [i32, i64, i64, i64]
+    L.moe_prepare_weights.restype = ctypes.c_int
+    L.moe_prepare_weights.argtypes = [i32, i64, i64, i64, vp, vp, vp]
+    L.moe_dequantize.restype = ctypes.c_int
+    L.moe_dequantize.argtypes = [i32, vp, i64, i64, i64, i64, i64, vp, vp, vp]
+    L.moe_route_workspace.restype = sz
+    L.moe_route_workspace.argtypes = [i32, i32, i32]
+    L.moe_route.restype = ctypes.c_int
+    L.moe_route.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_ffn_workspace.restype = sz
+    L.moe_expert_ffn_workspace.argtypes = [ctypes.POINTER(LayerDesc), i32]
+    L.moe_expert_ffn.restype = ctypes.c_int
+    L.moe_expert_ffn.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_combine.restype = ctypes.c_int
+    L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
+    if L.moe_abi_version() != ABI_VERSION:
+        raise ImportError(f"libmoe2bit ABI {L.moe_abi_version()} != binding ABI {ABI_VERSION}")
+    return L
+
+
+lib = _load()
+
+
+def _check(st: int):
+    if st != MOE_OK:
+        raise MoeError(st, lib.moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    if t.dtype == torch.float32:
+        return DT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# ----------------------------------------------------------------------------
+# C-ABI calls (same names)
+# ----------------------------------------------------------------------------
+def moe_abi_version() -> int:
+    return lib.moe_abi_version()
+
+
+def moe_last_error() -> str:
+    return lib.moe_last_error().decode()
+
+
+def moe_weight_bytes(fmt: int, n_mats: int, rows: int, cols: int) -> int:
+    return lib.moe_weight_bytes(fmt, n_mats, rows, cols)
+
+
+def moe_prepare_weights(fmt, n_mats, rows, cols, canonical, prepared, stream=None):
+    _check(lib.moe_prepare_weights(fmt, n_mats, rows, cols, _ptr(canonical), _ptr(prepared), _stream(stream)))
+
+
+def moe_dequantize(fmt, prepared, n_mats, rows, cols, mat_begin, mat_count, codebook, out, stream=None):
+    _check(lib.moe_dequantize(fmt, _ptr(prepared), n_mats, rows, cols, mat_begin, mat_count, _ptr(codebook),
+                              _ptr(out), _stream(stream)))
+
+
+def moe_route_workspace(n_tokens: int, n_experts: int, top_k: int) -> int:
+    return lib.moe_route_workspace(n_tokens, n_experts, top_k)
+
+
+def moe_route(x, w_router, n_experts, top_k, topk_idx, topk_w, expert_offsets, perm, active, ws, bias=None,
+              logits=None, stream=None):
+    T, H = x.shape
+    _check(lib.moe_route(_ptr(x), _dt(x), T, H, _ptr(w_router), _dt(w_router), n_experts, _ptr(bias), top_k,
+                         _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(expert_offsets), _ptr(perm), _ptr(active),
+                         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_expert_ffn_workspace(desc: LayerDesc, n_tokens: int) -> int:
+    return lib.moe_expert_ffn_workspace(ctypes.byref(desc), n_tokens)
+
+
+def moe_expert_ffn(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, slot_out, shared_out, ws, stream=None):
+    T = x.shape[0]
+    _check(lib.moe_expert_ffn(ctypes.byref(desc), _ptr(x), _dt(x), T, _ptr(topk_idx), _ptr(expert_offsets),
+                              _ptr(perm), _ptr(active), _ptr(slot_out), _ptr(shared_out), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_combine(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, y, stream=None):
+    _check(lib.moe_combine(_ptr(slot_out), _ptr(topk_w), _ptr(shared_out), n_tokens, top_k, hidden, _ptr(y),
+                           _stream(stream)))
+
+
+from .layer import DeviceLayer, LayerBuffers  # noqa: E402  (needs `lib` loaded)

@@ -1,0 +1,252 @@
+// C-ABI entry points of libmoe2bit: argument checking on the host, then kernel
+// dispatch on the caller's stream.  Nothing here allocates device memory or
+// synchronizes; no C++ exception crosses the interface.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe2bit.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+moe_status ok() {
+    g_err[0] = '\0';
+    return MOE_OK;
+}
+
+moe_status from_hip(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(MOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+int block_bytes(int fmt) {
+    switch (fmt) {
+        case MOE_FMT_IQ2X: return 66;
+        case MOE_FMT_Q2K: return 84;
+        case MOE_FMT_Q4K: return 144;
+        default: return 0;
+    }
+}
+
+// Sub-blocks may not straddle rows.
+int sub_len(int fmt) { return fmt == MOE_FMT_Q2K ? 16 : 32; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status check_matrix(int fmt, int64_t n_mats, int64_t rows, int64_t cols, const char *what) {
+    if (!block_bytes(fmt)) return fail(MOE_ERR_INVALID_ARG, "%s: unknown format %d", what, fmt);
+    if (n_mats < 1 || rows < 1 || cols < 1) return fail(MOE_ERR_INVALID_ARG, "%s: empty shape", what);
+    if ((rows * cols) % 256) return fail(MOE_ERR_INVALID_ARG, "%s: rows*cols not a multiple of 256", what);
+    if (cols % sub_len(fmt))
+        return fail(MOE_ERR_INVALID_ARG, "%s: cols %% %d != 0 (sub-blocks would straddle rows)", what, sub_len(fmt));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_last_error(void) { return g_err; }
+
+size_t moe_weight_bytes(int32_t fmt, int64_t n_mats, int64_t rows, int64_t cols) {
+    const int bb = block_bytes(fmt);
+    if (!bb || n_mats < 1 || rows < 1 || cols < 1 || (rows * cols) % 256) return 0;
+    return (size_t)(n_mats * rows * cols / 256) * (size_t)bb;
+}
+
+moe_status moe_prepare_weights(int32_t fmt, int64_t n_mats, int64_t rows, int64_t cols, const void *canonical,
+                               void *prepared, void *stream) {
+    moe_status st = check_matrix(fmt, n_mats, rows, cols, "moe_prepare_weights");
+    if (st != MOE_OK) return st;
+    if (!canonical || !prepared) return fail(MOE_ERR_INVALID_ARG, "moe_prepare_weights: null pointer");
+    if (!aligned(prepared, 16)) return fail(MOE_ERR_INVALID_ARG, "moe_prepare_weights: prepared not 16-byte aligned");
+    const size_t bytes = moe_weight_bytes(fmt, n_mats, rows, cols);
+    const char *c = static_cast<const char *>(canonical), *p = static_cast<const char *>(prepared);
+    if (c < p + bytes && p < c + bytes) return fail(MOE_ERR_INVALID_ARG, "moe_prepare_weights: buffers overlap");
+    const int64_t NB = n_mats * rows * cols / 256;
+    return from_hip(moe::launch_prepare(fmt, NB, canonical, prepared, (hipStream_t)stream), "moe_prepare_weights");
+}
+
+moe_status moe_dequantize(int32_t fmt, const void *prepared, int64_t n_mats, int64_t rows, int64_t cols,
+                          int64_t mat_begin, int64_t mat_count, const uint8_t *codebook, float *out, void *stream) {
+    moe_status st = check_matrix(fmt, n_mats, rows, cols, "moe_dequantize");
+    if (st != MOE_OK) return st;
+    if (!prepared || !out || (fmt == MOE_FMT_IQ2X && !codebook))
+        return fail(MOE_ERR_INVALID_ARG, "moe_dequantize: null pointer");
+    if (!aligned(prepared, 16) || !aligned(out, 4)) return fail(MOE_ERR_INVALID_ARG, "moe_dequantize: misaligned");
+    if (mat_begin < 0 || mat_count < 1 || mat_begin + mat_count > n_mats)
+        return fail(MOE_ERR_INVALID_ARG, "moe_dequantize: matrix range [%lld, +%lld) outside [0, %lld)",
+                    (long long)mat_begin, (long long)mat_count, (long long)n_mats);
+    if ((rows * cols) % 256) return fail(MOE_ERR_INVALID_ARG, "moe_dequantize: matrix not whole blocks");
+    const int64_t per = rows * cols / 256;
+    return from_hip(moe::launch_dequant(fmt, n_mats * per, mat_begin * per, mat_count * per, prepared, codebook, out,
+                                        (hipStream_t)stream),
+                    "moe_dequantize");
+}
+
+size_t moe_route_workspace(int32_t n_tokens, int32_t n_experts, int32_t top_k) {
+    (void)top_k;
+    if (n_tokens < 1 || n_experts < 1) return 0;
+    return ((size_t)n_tokens * n_experts * sizeof(float) + 255) / 256 * 256;
+}
+
+moe_status moe_route(const void *x, int32_t x_dt, int32_t n_tokens, int32_t hidden, const void *w_router,
+                     int32_t w_dt, int32_t n_experts, const float *bias, int32_t top_k, int32_t *topk_idx,
+                     float *topk_w, float *logits, int32_t *expert_offsets, int32_t *perm, int32_t *active, void *ws,
+                     size_t ws_bytes, void *stream) {
+    if (!x || !w_router || !topk_idx || !topk_w || !expert_offsets || !perm || !active || !ws)
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: null pointer");
+    if ((x_dt != MOE_DT_F32 && x_dt != MOE_DT_BF16) || (w_dt != MOE_DT_F32 && w_dt != MOE_DT_BF16))
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: unknown dtype");
+    if (n_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "moe_route: n_tokens < 1");
+    if (hidden < 64 || hidden % 64) return fail(MOE_ERR_INVALID_ARG, "moe_route: hidden %% 64 != 0");
+    if (n_experts < 1 || n_experts > 256) return fail(MOE_ERR_INVALID_ARG, "moe_route: n_experts outside [1, 256]");
+    if (top_k < 1 || top_k > n_experts) return fail(MOE_ERR_INVALID_ARG, "moe_route: top_k outside [1, n_experts]");
+    if ((int64_t)n_tokens * top_k > (int64_t)1 << 30) return fail(MOE_ERR_INVALID_ARG, "moe_route: too many slots");
+    if (ws_bytes < moe_route_workspace(n_tokens, n_experts, top_k))
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: workspace too small (%zu < %zu)", ws_bytes,
+                    moe_route_workspace(n_tokens, n_experts, top_k));
+    if (!aligned(ws, 16) || !aligned(x, 4) || !aligned(w_router, 4))
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: misaligned pointer");
+    moe::RouteArgs a;
+    a.x = x; a.x_bf16 = x_dt == MOE_DT_BF16; a.T = n_tokens; a.H = hidden;
+    a.w = w_router; a.w_bf16 = w_dt == MOE_DT_BF16; a.E = n_experts; a.bias = bias; a.k = top_k;
+    a.topk_idx = topk_idx; a.topk_w = topk_w; a.logits_out = logits;
+    a.offsets = expert_offsets; a.perm = perm; a.active = active;
+    a.logits_ws = static_cast<float *>(ws);
+    return from_hip(moe::launch_route(a, (hipStream_t)stream), "moe_route");
+}
+
+static moe_status check_layer(const moe_layer_desc *L, const char *fn) {
+    if (!L) return fail(MOE_ERR_INVALID_ARG, "%s: null layer", fn);
+    if (L->hidden < 1 || L->inter < 1) return fail(MOE_ERR_INVALID_ARG, "%s: bad shape", fn);
+    if (L->n_experts < 1 || L->n_experts > 256) return fail(MOE_ERR_INVALID_ARG, "%s: n_experts outside [1, 256]", fn);
+    if (L->top_k < 1 || L->top_k > L->n_experts) return fail(MOE_ERR_INVALID_ARG, "%s: top_k outside [1, E]", fn);
+    if (L->gate_up_fmt != MOE_FMT_IQ2X && L->gate_up_fmt != MOE_FMT_Q4K)
+        return fail(MOE_ERR_INVALID_ARG, "%s: gate/up format must be iq2x or q4k", fn);
+    if (L->down_fmt != MOE_FMT_Q2K && L->down_fmt != MOE_FMT_Q4K)
+        return fail(MOE_ERR_INVALID_ARG, "%s: down format must be q2k or q4k", fn);
+    moe_status st = check_matrix(L->gate_up_fmt, L->n_experts, L->inter, L->hidden, fn);
+    if (st != MOE_OK) return st;
+    if ((st = check_matrix(L->down_fmt, L->n_experts, L->hidden, L->inter, fn)) != MOE_OK) return st;
+    if (!L->gate || !L->up || !L->down) return fail(MOE_ERR_INVALID_ARG, "%s: null expert weights", fn);
+    if (!aligned(L->gate, 16) || !aligned(L->up, 16) || !aligned(L->down, 16))
+        return fail(MOE_ERR_INVALID_ARG, "%s: expert weights not 16-byte aligned", fn);
+    if (L->gate_up_fmt == MOE_FMT_IQ2X && !L->codebook) return fail(MOE_ERR_INVALID_ARG, "%s: null codebook", fn);
+    if (L->shared_inter < 0) return fail(MOE_ERR_INVALID_ARG, "%s: shared_inter < 0", fn);
+    if (L->shared_inter > 0) {
+        if (!L->shared_gate || !L->shared_up || !L->shared_down)
+            return fail(MOE_ERR_INVALID_ARG, "%s: null shared expert weights", fn);
+        if (!aligned(L->shared_gate, 16) || !aligned(L->shared_up, 16) || !aligned(L->shared_down, 16))
+            return fail(MOE_ERR_INVALID_ARG, "%s: shared expert weights not 16-byte aligned", fn);
+        if (L->hidden % 8 || L->shared_inter % 8)
+            return fail(MOE_ERR_INVALID_ARG, "%s: shared expert dims must be multiples of 8", fn);
+    }
+    if (L->path < MOE_PATH_AUTO || L->path > MOE_PATH_GEMM) return fail(MOE_ERR_INVALID_ARG, "%s: unknown path", fn);
+    return MOE_OK;
+}
+
+static moe::FfnArgs make_args(const moe_layer_desc *L, const void *x, int x_dt, int T) {
+    moe::FfnArgs a;
+    memset(&a, 0, sizeof a);
+    a.H = L->hidden; a.I = L->inter; a.E = L->n_experts; a.k = L->top_k; a.T = T;
+    a.fmt_gu = L->gate_up_fmt; a.fmt_d = L->down_fmt;
+    a.gate = static_cast<const uint8_t *>(L->gate);
+    a.up = static_cast<const uint8_t *>(L->up);
+    a.down = static_cast<const uint8_t *>(L->down);
+    a.codebook = L->codebook;
+    a.Is = L->shared_inter;
+    a.sg = static_cast<const uint16_t *>(L->shared_gate);
+    a.su = static_cast<const uint16_t *>(L->shared_up);
+    a.sd = static_cast<const uint16_t *>(L->shared_down);
+    a.x = x; a.x_bf16 = x_dt == MOE_DT_BF16;
+    return a;
+}
+
+// Kernel family for this call: 1 generic, 2 gemv, 3 gemm.
+static int choose_path(const moe_layer_desc *L, const moe::FfnArgs &a) {
+    if (L->path != MOE_PATH_AUTO) return L->path;
+    if (a.T <= 4 && moe::ffn_gemv_supported(a)) return MOE_PATH_GEMV;
+    if (a.T > 4 && moe::ffn_gemm_supported(a)) return MOE_PATH_GEMM;
+    return MOE_PATH_GENERIC;
+}
+
+static size_t workspace_for(int path, const moe_layer_desc *L, int32_t T) {
+    const int Is = L->shared_inter;
+    switch (path) {
+        case MOE_PATH_GEMV: return moe::ffn_workspace_gemv(L->hidden, L->inter, L->n_experts, L->top_k, Is, T);
+        case MOE_PATH_GEMM: return moe::ffn_workspace_gemm(L->hidden, L->inter, L->n_experts, L->top_k, Is, T);
+        default: return moe::ffn_workspace_generic(L->hidden, L->inter, L->n_experts, L->top_k, Is, T);
+    }
+}
+
+size_t moe_expert_ffn_workspace(const moe_layer_desc *L, int32_t n_tokens) {
+    if (n_tokens < 1 || check_layer(L, "moe_expert_ffn_workspace") != MOE_OK) return 0;
+    size_t m = 0;
+    for (int p = MOE_PATH_GENERIC; p <= MOE_PATH_GEMM; ++p) {
+        size_t b = workspace_for(p, L, n_tokens);
+        if (b > m) m = b;
+    }
+    return m;
+}
+
+moe_status moe_expert_ffn(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
+                          const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
+                          const int32_t *active, float *slot_out, float *shared_out, void *ws, size_t ws_bytes,
+                          void *stream) {
+    moe_status st = check_layer(L, "moe_expert_ffn");
+    if (st != MOE_OK) return st;
+    if (!x || !topk_idx || !expert_offsets || !perm || !active || !slot_out || !ws)
+        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: null pointer");
+    if (x_dt != MOE_DT_F32 && x_dt != MOE_DT_BF16) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: unknown dtype");
+    if (n_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: n_tokens < 1");
+    if ((L->shared_inter > 0) != (shared_out != nullptr))
+        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: shared_out must be given iff the layer has a shared expert");
+    if (!aligned(x, 16) || !aligned(slot_out, 16) || !aligned(ws, 256) || (shared_out && !aligned(shared_out, 16)))
+        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: misaligned pointer (x/outputs 16 B, ws 256 B)");
+    moe::FfnArgs a = make_args(L, x, x_dt, n_tokens);
+    a.topk_idx = topk_idx; a.offsets = expert_offsets; a.perm = perm; a.active = active;
+    a.slot_out = slot_out; a.shared_out = shared_out; a.ws = ws;
+    const int path = choose_path(L, a);
+    if (path == MOE_PATH_GEMV && !(moe::ffn_gemv_supported(a)))
+        return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: decode kernels need bf16 x, iq2x/q2k, T <= 4 and "
+                                         "hidden in {512..4096}, supported inter/shared sizes");
+    if (path == MOE_PATH_GEMM && !(moe::ffn_gemm_supported(a)))
+        return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: grouped-GEMM kernels need bf16 x and hidden, inter, "
+                                         "shared_inter multiples of 256");
+    const size_t need = workspace_for(path, L, n_tokens);
+    if (ws_bytes < need)
+        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: workspace too small (%zu < %zu)", ws_bytes, need);
+    hipError_t e;
+    if (path == MOE_PATH_GEMV) e = moe::launch_ffn_gemv(a, (hipStream_t)stream);
+    else if (path == MOE_PATH_GEMM) e = moe::launch_ffn_gemm(a, (hipStream_t)stream);
+    else e = moe::launch_ffn_generic(a, (hipStream_t)stream);
+    return from_hip(e, "moe_expert_ffn");
+}
+
+moe_status moe_combine(const float *slot_out, const float *topk_w, const float *shared_out, int32_t n_tokens,
+                       int32_t top_k, int32_t hidden, float *y, void *stream) {
+    if (!slot_out || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "moe_combine: null pointer");
+    if (n_tokens < 1 || top_k < 1 || hidden < 1) return fail(MOE_ERR_INVALID_ARG, "moe_combine: bad shape");
+    if (!aligned(slot_out, 4) || !aligned(y, 4) || !aligned(topk_w, 4))
+        return fail(MOE_ERR_INVALID_ARG, "moe_combine: misaligned pointer");
+    return from_hip(moe::launch_combine(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, y, (hipStream_t)stream),
+                    "moe_combine");
+}
+
+}  // extern "C"

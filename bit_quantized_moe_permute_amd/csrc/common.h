@@ -1,0 +1,160 @@
+// Device-side helpers shared by the kernels of libmoe2bit (gfx950 only).
+//
+// Prepared (device) layouts.  A stack of NB blocks (NB = n_mats*rows*cols/256)
+// is stored as structure-of-arrays regions so that every 16-byte lane load
+// lands on whole fields:
+//
+//  iq2x  Q: NB x 64 B, then D: NB x fp16.
+//        Block b's 64 bytes are four 16-byte chunks; chunk c holds the eight
+//        16-bit sub-group fields of groups c and c+4 (fields 0..3 = group c,
+//        sub-groups 0..3; fields 4..7 = group c+4).  A sub-group field is
+//          bits 0..7  codebook row, bits 8..14 the seven stored signs,
+//          bit 15     bit p of the group's 4-bit scale s (p = sub-group).
+//        A lane that loads one chunk therefore owns two complete groups.
+//  q2k   Q: NB x 64 B, S: NB x 16 B, D: NB x u32 (d | dmin << 16).
+//        Chunk c (16 B) = sub-blocks 4c..4c+3, one dword each; in the dword of
+//        sub-block j, nibble i carries q[16j+i] in bits 0..1 and q[16j+8+i] in
+//        bits 2..3, so (v & 0x33333333) and ((v >> 2) & 0x33333333) are eight
+//        fp4 codes each.  S keeps the canonical (sc | m << 4) bytes.
+//  q4k   Q: NB x 128 B (canonical nibble order: 16 B per 32-weight sub-block),
+//        M: NB x 16 B = d | dmin | u32 low nibbles of fields 0..7 | u32 low
+//        nibbles of fields 8..15 | u32 top two bits of field f at bits 2f.
+//
+// fp4 (E2M1) codes: a 2- or 4-bit unsigned integer code q placed in a nibble
+// decodes to q/2 (codes 0..3: 0, 0.5, 1, 1.5); iq2x magnitudes 1, 2, 3 are the
+// codes 0x2, 0x4, 0x5, and bit 3 is the sign.  The hardware converts two codes
+// at a time to bf16/f16/f32 pairs (v_cvt_scalef32_pk_*_fp4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+#define MOE_QK 256
+
+namespace moe {
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)h);
+    return (float)v;
+}
+
+// fp4 code of an iq2x magnitude (1 -> 1.0, 2 -> 2.0, 3 -> 3.0).
+__device__ __forceinline__ uint32_t mag_to_fp4(uint32_t c) { return c == 1 ? 0x2u : (c == 2 ? 0x4u : 0x5u); }
+
+// Eight codebook magnitudes of row e as eight fp4 codes (nibble i = weight i).
+__device__ __forceinline__ uint32_t codebook_row_fp4(const uint8_t *cb, int e) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= mag_to_fp4(cb[8 * e + i]) << (4 * i);
+    return w;
+}
+
+// Sign bits of an 8-weight sub-group spread onto fp4 sign positions (bit 4i+3);
+// the eighth sign is the parity of the seven stored ones.
+__device__ __forceinline__ uint32_t sign_spread(uint32_t s7) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) w |= ((s7 >> i) & 1u) << (4 * i + 3);
+    w |= (uint32_t)(__builtin_popcount(s7) & 1) << 31;
+    return w;
+}
+
+// Two fp4 codes (byte `sel` of v) -> bf16 / f16 / f32 pairs, unscaled.
+template <int SEL> __device__ __forceinline__ bf16x2_t fp4x2_bf16(uint32_t v) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, SEL);
+}
+template <int SEL> __device__ __forceinline__ f16x2_t fp4x2_f16(uint32_t v) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, SEL);
+}
+template <int SEL> __device__ __forceinline__ f32x2_t fp4x2_f32(uint32_t v) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, SEL);
+}
+
+__device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+__device__ __forceinline__ float dot2_f16(f16x2_t a, f16x2_t b, float c) {
+    return __builtin_amdgcn_fdot2(a, b, c, false);
+}
+
+// Wave-wide (64 lanes) sum.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// q4k field f (6 bits) from the prepared 16-byte meta record.
+__device__ __forceinline__ uint32_t q4k_field(uint32_t lo8, uint32_t hi8, uint32_t top, int f) {
+    uint32_t nib = f < 8 ? (lo8 >> (4 * f)) & 15u : (hi8 >> (4 * (f - 8))) & 15u;
+    return nib | (((top >> (2 * f)) & 3u) << 4);
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Scalar-path decoders of the prepared layouts (used by the generic kernels).
+// NB is the block count of the whole stack; bl a block index in the stack.
+// cb4 / sgn are the fp4 codebook rows and spread sign words (LDS tables).
+// ---------------------------------------------------------------------------
+
+// Eight weights of sub-group sg (0..31) of iq2x block bl, exact.
+__device__ __forceinline__ void iq2x_sub8(const uint8_t *prep, int64_t NB, int64_t bl, int sg, const uint32_t *cb4,
+                                          const uint32_t *sgn, float w[8]) {
+    const int g = sg >> 2, p = sg & 3;
+    const uint16_t *F = reinterpret_cast<const uint16_t *>(prep + bl * 64) + (g & 3) * 8 + (g >> 2) * 4;
+    uint32_t s = ((F[0] >> 15) & 1u) | (((F[1] >> 15) & 1u) << 1) | (((F[2] >> 15) & 1u) << 2) |
+                 (((F[3] >> 15) & 1u) << 3);
+    uint32_t f = F[p];
+    float S = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(prep + NB * 64)[bl]) * (float)(2 * s + 1);
+    uint32_t word = cb4[f & 0xFF] | sgn[(f >> 8) & 0x7F];
+    f32x2_t a = fp4x2_f32<0>(word), b = fp4x2_f32<1>(word), c = fp4x2_f32<2>(word), d = fp4x2_f32<3>(word);
+    w[0] = S * a.x; w[1] = S * a.y; w[2] = S * b.x; w[3] = S * b.y;
+    w[4] = S * c.x; w[5] = S * c.y; w[6] = S * d.x; w[7] = S * d.y;
+}
+
+// Sixteen weights of sub-block j (0..15) of q2k block bl, exact.
+__device__ __forceinline__ void q2k_sub16(const uint8_t *prep, int64_t NB, int64_t bl, int j, float w[16]) {
+    uint32_t v = reinterpret_cast<const uint32_t *>(prep + bl * 64)[j];
+    uint32_t sm = prep[NB * 64 + bl * 16 + j];
+    uint32_t dd = reinterpret_cast<const uint32_t *>(prep + NB * 80)[bl];
+    float sc = 2.0f * f16_bits_to_f32(dd & 0xFFFF) * (float)(sm & 15u);   // codes decode to q/2
+    float mn = f16_bits_to_f32(dd >> 16) * (float)(sm >> 4);
+    uint32_t lo = v & 0x33333333u, hi = (v >> 2) & 0x33333333u;
+    f32x2_t a;
+    a = fp4x2_f32<0>(lo); w[0] = sc * a.x - mn; w[1] = sc * a.y - mn;
+    a = fp4x2_f32<1>(lo); w[2] = sc * a.x - mn; w[3] = sc * a.y - mn;
+    a = fp4x2_f32<2>(lo); w[4] = sc * a.x - mn; w[5] = sc * a.y - mn;
+    a = fp4x2_f32<3>(lo); w[6] = sc * a.x - mn; w[7] = sc * a.y - mn;
+    a = fp4x2_f32<0>(hi); w[8] = sc * a.x - mn; w[9] = sc * a.y - mn;
+    a = fp4x2_f32<1>(hi); w[10] = sc * a.x - mn; w[11] = sc * a.y - mn;
+    a = fp4x2_f32<2>(hi); w[12] = sc * a.x - mn; w[13] = sc * a.y - mn;
+    a = fp4x2_f32<3>(hi); w[14] = sc * a.x - mn; w[15] = sc * a.y - mn;
+}
+
+// Eight weights of 8-weight unit u (0..31) of q4k block bl, exact.
+__device__ __forceinline__ void q4k_sub8(const uint8_t *prep, int64_t NB, int64_t bl, int u, float w[8]) {
+    uint32_t v = reinterpret_cast<const uint32_t *>(prep + bl * 128)[u];
+    const uint32_t *M = reinterpret_cast<const uint32_t *>(prep + NB * 128 + bl * 16);
+    const int j = u >> 2;
+    float sc = f16_bits_to_f32(M[0] & 0xFFFF) * (float)q4k_field(M[1], M[2], M[3], j);
+    float mn = f16_bits_to_f32(M[0] >> 16) * (float)q4k_field(M[1], M[2], M[3], 8 + j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = sc * (float)((v >> (4 * i)) & 15u) - mn;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+}  // namespace moe

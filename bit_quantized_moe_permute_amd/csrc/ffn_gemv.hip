@@ -1,0 +1,538 @@
+// Decode / verify expert FFN: GEMV kernels for at most 4 tokens per expert.
+//
+// Each selected expert's weights are streamed once per call with 16-byte
+// lane loads.  A lane always covers the same columns, so the activations (x
+// for gate/up, h for down) are loaded once into registers and reused for every
+// row; only the 2-bit fields move per row.  Weights are decoded in registers:
+// an iq2x sub-group (8 weights) is one LDS lookup of its codebook row as eight
+// fp4 codes, OR-ed with its spread sign word, then converted two at a time to
+// bf16 pairs (magnitudes 1..3, exact) and dotted with bf16 activation pairs;
+// the group scale (2s+1) and block scale d multiply the partial sums in fp32.
+// q2k codes are fp4 codes already (value q/2) and dot with fp16 h pairs; the
+// sub-block mins use per-sub-block sums of h.  Rows reduce across their lanes.
+//
+// The routed experts and the shared expert run in the same launch (different
+// workgroups), so the HBM-heavy bf16 shared rows and the VALU-heavy 2-bit rows
+// share the machine.
+#include "common.h"
+#include "internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int WAVES = 4;
+
+// rows per wave for bf16 rows with CPL 16-byte chunks per lane
+template <int CPL> constexpr int shared_nr() { return CPL >= 4 ? 1 : 4 / CPL; }
+
+template <int LPR> __device__ __forceinline__ float row_sum(float v) {
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ void tables(const uint8_t *codebook, uint32_t *cb4, uint32_t *sgn) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) cb4[i] = codebook_row_fp4(codebook, i);
+    for (int i = threadIdx.x; i < 128; i += blockDim.x) sgn[i] = sign_spread(i);
+}
+
+// Tokens of work item: routed expert (slots from the permutation) or all T (shared).
+template <int MAXM> struct Tokens {
+    int n;
+    int slot[MAXM];
+    int tok[MAXM];
+};
+
+// ---------------------------------------------------------------------------
+// iq2x: one 16-byte chunk = groups c and c+4 of one block (64 weights)
+// ---------------------------------------------------------------------------
+template <int MAXM>
+__device__ __forceinline__ void iq2x_chunk(uint4 q, float d, const uint32_t (&xr)[MAXM][32], const uint32_t *cb4,
+                                           const uint32_t *sgn, float (&acc)[MAXM]) {
+    float racc[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) racc[m] = 0.f;
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+        const uint32_t lo = grp ? q.z : q.x, hi = grp ? q.w : q.y;
+        const uint32_t s = ((lo >> 15) & 1u) | ((lo >> 30) & 2u) | ((hi >> 13) & 4u) | ((hi >> 28) & 8u);
+        float gacc[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) gacc[m] = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t f = ((p < 2 ? lo : hi) >> (16 * (p & 1))) & 0xFFFFu;
+            const uint32_t word = cb4[f & 0xFFu] | sgn[(f >> 8) & 0x7Fu];
+            const bf16x2_t w0 = fp4x2_bf16<0>(word), w1 = fp4x2_bf16<1>(word);
+            const bf16x2_t w2 = fp4x2_bf16<2>(word), w3 = fp4x2_bf16<3>(word);
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+                const uint32_t *xp = &xr[m][grp * 16 + p * 4];
+                float g = gacc[m];
+                g = dot2_bf16(w0, __builtin_bit_cast(bf16x2_t, xp[0]), g);
+                g = dot2_bf16(w1, __builtin_bit_cast(bf16x2_t, xp[1]), g);
+                g = dot2_bf16(w2, __builtin_bit_cast(bf16x2_t, xp[2]), g);
+                g = dot2_bf16(w3, __builtin_bit_cast(bf16x2_t, xp[3]), g);
+                gacc[m] = g;
+            }
+        }
+        const float mult = (float)(2 * s + 1);
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) racc[m] = __fmaf_rn(mult, gacc[m], racc[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) acc[m] = __fmaf_rn(d, racc[m], acc[m]);
+}
+
+// Routed gate/up for one expert and a tile of rows.  Row length H = 64*LPR*CPL.
+template <int LPR, int CPL, int MAXM, int NR>
+__device__ void routed_gateup(const FfnArgs &a, int e, const Tokens<MAXM> &tk, int row0, const uint32_t *cb4,
+                              const uint32_t *sgn, _Float16 *__restrict__ h) {
+    constexpr int RPI = 64 / LPR;                 // rows per wave iteration
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int cp = lane % LPR, rsub = lane / LPR;
+    const int H = a.H, I = a.I;
+    const int64_t nb_row = H / MOE_QK, nb_mat = (int64_t)I * nb_row, NB = nb_mat * a.E;
+    // activations for this lane's chunks, bf16 pairs
+    uint32_t xr[CPL][MAXM][32];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int ch = cp + LPR * i, b = ch >> 2, c = ch & 3;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const int t = tk.tok[m < tk.n ? m : 0];
+            const uint4 *xa = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + (int64_t)t * H +
+                                                              MOE_QK * b + 32 * c);
+            const uint4 *xb = xa + 16;            // +128 bf16: group c+4
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                uint4 u = xa[v];
+                xr[i][m][4 * v + 0] = u.x; xr[i][m][4 * v + 1] = u.y; xr[i][m][4 * v + 2] = u.z; xr[i][m][4 * v + 3] = u.w;
+                u = xb[v];
+                xr[i][m][16 + 4 * v + 0] = u.x; xr[i][m][16 + 4 * v + 1] = u.y;
+                xr[i][m][16 + 4 * v + 2] = u.z; xr[i][m][16 + 4 * v + 3] = u.w;
+            }
+        }
+    }
+    const uint8_t *Gq = a.gate, *Uq = a.up;
+    const uint16_t *Gd = reinterpret_cast<const uint16_t *>(a.gate + NB * 64);
+    const uint16_t *Ud = reinterpret_cast<const uint16_t *>(a.up + NB * 64);
+    uint4 gq[NR][CPL], uq[NR][CPL];
+    uint16_t gd[NR][CPL], ud[NR][CPL];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        const int r = min(row0 + (wv * NR + j) * RPI + rsub, I - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int ch = cp + LPR * i;
+            const int64_t bl = (int64_t)e * nb_mat + (int64_t)r * nb_row + (ch >> 2);
+            gq[j][i] = *reinterpret_cast<const uint4 *>(Gq + bl * 64 + (ch & 3) * 16);
+            uq[j][i] = *reinterpret_cast<const uint4 *>(Uq + bl * 64 + (ch & 3) * 16);
+            gd[j][i] = Gd[bl];
+            ud[j][i] = Ud[bl];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        float ga[MAXM], ua[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) { ga[m] = 0.f; ua[m] = 0.f; }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            iq2x_chunk<MAXM>(gq[j][i], f16_bits_to_f32(gd[j][i]), xr[i], cb4, sgn, ga);
+            iq2x_chunk<MAXM>(uq[j][i], f16_bits_to_f32(ud[j][i]), xr[i], cb4, sgn, ua);
+        }
+        const int r = row0 + (wv * NR + j) * RPI + rsub;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const float g = row_sum<LPR>(ga[m]), u = row_sum<LPR>(ua[m]);
+            if (m < tk.n && cp == 0 && r < I) h[(int64_t)tk.slot[m] * I + r] = (_Float16)silu_mul(g, u);
+        }
+    }
+}
+
+// Shared gate/up (bf16 rows of H = 8*LPR*CPL).
+template <int LPR, int CPL, int MAXM, int NR>
+__device__ void shared_gateup(const FfnArgs &a, const Tokens<MAXM> &tk, int row0, float *__restrict__ hs) {
+    constexpr int RPI = 64 / LPR;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int cp = lane % LPR, rsub = lane / LPR;
+    const int H = a.H, Is = a.Is;
+    uint32_t xr[CPL][MAXM][4];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const int t = tk.tok[m < tk.n ? m : 0];
+            const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + (int64_t)t * H +
+                                                            8 * (cp + LPR * i));
+            xr[i][m][0] = u.x; xr[i][m][1] = u.y; xr[i][m][2] = u.z; xr[i][m][3] = u.w;
+        }
+    uint4 gq[NR][CPL], uq[NR][CPL];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        const int r = min(row0 + (wv * NR + j) * RPI + rsub, Is - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            gq[j][i] = *reinterpret_cast<const uint4 *>(a.sg + (int64_t)r * H + 8 * (cp + LPR * i));
+            uq[j][i] = *reinterpret_cast<const uint4 *>(a.su + (int64_t)r * H + 8 * (cp + LPR * i));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        float ga[MAXM], ua[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) { ga[m] = 0.f; ua[m] = 0.f; }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const uint32_t g4[4] = {gq[j][i].x, gq[j][i].y, gq[j][i].z, gq[j][i].w};
+            const uint32_t u4[4] = {uq[j][i].x, uq[j][i].y, uq[j][i].z, uq[j][i].w};
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const bf16x2_t xv = __builtin_bit_cast(bf16x2_t, xr[i][m][v]);
+                    ga[m] = dot2_bf16(__builtin_bit_cast(bf16x2_t, g4[v]), xv, ga[m]);
+                    ua[m] = dot2_bf16(__builtin_bit_cast(bf16x2_t, u4[v]), xv, ua[m]);
+                }
+        }
+        const int r = row0 + (wv * NR + j) * RPI + rsub;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const float g = row_sum<LPR>(ga[m]), u = row_sum<LPR>(ua[m]);
+            if (m < tk.n && cp == 0 && r < Is) hs[(int64_t)tk.tok[m] * Is + r] = silu_mul(g, u);
+        }
+    }
+}
+
+template <int MAXM>
+__device__ __forceinline__ bool routed_tokens(const FfnArgs &a, int ai, int &e, Tokens<MAXM> &tk) {
+    if (ai >= a.active[0]) return false;
+    e = a.active[1 + ai];
+    const int o0 = a.offsets[e];
+    tk.n = min(a.offsets[e + 1] - o0, MAXM);
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        const int s = a.perm[o0 + (m < tk.n ? m : 0)];
+        tk.slot[m] = s;
+        tk.tok[m] = s / a.k;
+    }
+    return true;
+}
+
+template <int MAXM> __device__ __forceinline__ void all_tokens(const FfnArgs &a, Tokens<MAXM> &tk) {
+    tk.n = min(a.T, MAXM);
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        tk.tok[m] = m < tk.n ? m : 0;
+        tk.slot[m] = tk.tok[m];
+    }
+}
+
+template <int LPR, int CPL, int SLPR, int SCPL, int MAXM, int NR>
+__global__ __launch_bounds__(256) void k_gemv_gateup(FfnArgs a, int wgs_per_expert, int n_routed_wgs,
+                                                      _Float16 *__restrict__ h, float *__restrict__ hs) {
+    __shared__ uint32_t cb4[256], sgn[128];
+    const int bid = blockIdx.x;
+    if (bid < n_routed_wgs) {
+        tables(a.codebook, cb4, sgn);
+        __syncthreads();
+        int e;
+        Tokens<MAXM> tk;
+        if (!routed_tokens<MAXM>(a, bid / wgs_per_expert, e, tk)) return;
+        constexpr int ROWS = WAVES * NR * (64 / LPR);
+        routed_gateup<LPR, CPL, MAXM, NR>(a, e, tk, (bid % wgs_per_expert) * ROWS, cb4, sgn, h);
+    } else {
+        Tokens<MAXM> tk;
+        all_tokens<MAXM>(a, tk);
+        constexpr int SNR = shared_nr<SCPL>();
+        constexpr int ROWS = WAVES * SNR * (64 / SLPR);
+        shared_gateup<SLPR, SCPL, MAXM, SNR>(a, tk, (bid - n_routed_wgs) * ROWS, hs);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// down projection
+// ---------------------------------------------------------------------------
+// q2k chunk (16 B = sub-blocks 4c..4c+3, 64 weights) against fp16 h pairs.
+template <int MAXM>
+__device__ __forceinline__ void q2k_chunk(uint4 q, uint32_t sm4, uint32_t dd, const uint32_t (&hr)[MAXM][32],
+                                          const float (&hsum)[MAXM][4], float (&acc)[MAXM]) {
+    float sacc[MAXM], macc[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) { sacc[m] = 0.f; macc[m] = 0.f; }
+    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t lo = qw[jj] & 0x33333333u, hi = (qw[jj] >> 2) & 0x33333333u;
+        const f16x2_t w0 = fp4x2_f16<0>(lo), w1 = fp4x2_f16<1>(lo), w2 = fp4x2_f16<2>(lo), w3 = fp4x2_f16<3>(lo);
+        const f16x2_t w4 = fp4x2_f16<0>(hi), w5 = fp4x2_f16<1>(hi), w6 = fp4x2_f16<2>(hi), w7 = fp4x2_f16<3>(hi);
+        const float sc = (float)((sm4 >> (8 * jj)) & 15u), mn = (float)((sm4 >> (8 * jj + 4)) & 15u);
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const uint32_t *hp = &hr[m][8 * jj];
+            float p = 0.f;
+            p = dot2_f16(w0, __builtin_bit_cast(f16x2_t, hp[0]), p);
+            p = dot2_f16(w1, __builtin_bit_cast(f16x2_t, hp[1]), p);
+            p = dot2_f16(w2, __builtin_bit_cast(f16x2_t, hp[2]), p);
+            p = dot2_f16(w3, __builtin_bit_cast(f16x2_t, hp[3]), p);
+            p = dot2_f16(w4, __builtin_bit_cast(f16x2_t, hp[4]), p);
+            p = dot2_f16(w5, __builtin_bit_cast(f16x2_t, hp[5]), p);
+            p = dot2_f16(w6, __builtin_bit_cast(f16x2_t, hp[6]), p);
+            p = dot2_f16(w7, __builtin_bit_cast(f16x2_t, hp[7]), p);
+            sacc[m] = __fmaf_rn(sc, p, sacc[m]);
+            macc[m] = __fmaf_rn(mn, hsum[m][jj], macc[m]);
+        }
+    }
+    const float d2 = 2.0f * f16_bits_to_f32(dd & 0xFFFFu), dmin = f16_bits_to_f32(dd >> 16);
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) acc[m] += d2 * sacc[m] - dmin * macc[m];
+}
+
+// Loads this lane's 64 h values of chunk ch (f16) in the order q2k_chunk uses:
+// sub-block jj pairs: (i, i+1) for i = 0,2,4,6 then (8+i, 9+i).
+template <int MAXM>
+__device__ __forceinline__ void load_h_chunk(const _Float16 *h, int I, const Tokens<MAXM> &tk, int ch,
+                                             uint32_t (&hr)[MAXM][32], float (&hsum)[MAXM][4]) {
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        const int s = tk.slot[m < tk.n ? m : 0];
+        const uint4 *hp = reinterpret_cast<const uint4 *>(h + (int64_t)s * I + 64 * ch);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const uint4 u = hp[v];
+            hr[m][4 * v + 0] = u.x; hr[m][4 * v + 1] = u.y; hr[m][4 * v + 2] = u.z; hr[m][4 * v + 3] = u.w;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            float sum = 0.f;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const f16x2_t p = __builtin_bit_cast(f16x2_t, hr[m][8 * jj + v]);
+                sum += (float)p.x + (float)p.y;
+            }
+            hsum[m][jj] = sum;
+        }
+    }
+}
+
+template <int LPR, int CPL, int MAXM, int NR>
+__device__ void routed_down(const FfnArgs &a, int e, const Tokens<MAXM> &tk, int row0, const _Float16 *__restrict__ h) {
+    constexpr int RPI = 64 / LPR;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int cp = lane % LPR, rsub = lane / LPR;
+    const int H = a.H, I = a.I;
+    const int64_t nb_row = I / MOE_QK, nb_mat = (int64_t)H * nb_row, NB = nb_mat * a.E;
+    uint32_t hr[CPL][MAXM][32];
+    float hsum[CPL][MAXM][4];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) load_h_chunk<MAXM>(h, I, tk, cp + LPR * i, hr[i], hsum[i]);
+    const uint8_t *Q = a.down;
+    const uint8_t *S = a.down + NB * 64;
+    const uint32_t *D = reinterpret_cast<const uint32_t *>(a.down + NB * 80);
+    uint4 q[NR][CPL];
+    uint32_t sm[NR][CPL], dd[NR][CPL];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        const int r = min(row0 + (wv * NR + j) * RPI + rsub, H - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int ch = cp + LPR * i;
+            const int64_t bl = (int64_t)e * nb_mat + (int64_t)r * nb_row + (ch >> 2);
+            q[j][i] = *reinterpret_cast<const uint4 *>(Q + bl * 64 + (ch & 3) * 16);
+            sm[j][i] = *reinterpret_cast<const uint32_t *>(S + bl * 16 + (ch & 3) * 4);
+            dd[j][i] = D[bl];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        float acc[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) acc[m] = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) q2k_chunk<MAXM>(q[j][i], sm[j][i], dd[j][i], hr[i], hsum[i], acc);
+        const int r = row0 + (wv * NR + j) * RPI + rsub;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const float o = row_sum<LPR>(acc[m]);
+            if (m < tk.n && cp == 0 && r < H) a.slot_out[(int64_t)tk.slot[m] * H + r] = o;
+        }
+    }
+}
+
+// Shared down: bf16 rows of Is = 8*LPR*CPL against fp32 h.
+template <int LPR, int CPL, int MAXM, int NR>
+__device__ void shared_down(const FfnArgs &a, const Tokens<MAXM> &tk, int row0, const float *__restrict__ hs) {
+    constexpr int RPI = 64 / LPR;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int cp = lane % LPR, rsub = lane / LPR;
+    const int H = a.H, Is = a.Is;
+    float hr[CPL][MAXM][8];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const float4 *p = reinterpret_cast<const float4 *>(hs + (int64_t)tk.tok[m < tk.n ? m : 0] * Is +
+                                                               8 * (cp + LPR * i));
+            const float4 u = p[0], v = p[1];
+            hr[i][m][0] = u.x; hr[i][m][1] = u.y; hr[i][m][2] = u.z; hr[i][m][3] = u.w;
+            hr[i][m][4] = v.x; hr[i][m][5] = v.y; hr[i][m][6] = v.z; hr[i][m][7] = v.w;
+        }
+    uint4 q[NR][CPL];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        const int r = min(row0 + (wv * NR + j) * RPI + rsub, H - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            q[j][i] = *reinterpret_cast<const uint4 *>(a.sd + (int64_t)r * Is + 8 * (cp + LPR * i));
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        float acc[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) acc[m] = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const uint32_t w4[4] = {q[j][i].x, q[j][i].y, q[j][i].z, q[j][i].w};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float wl = __uint_as_float(w4[v] << 16), wh = __uint_as_float(w4[v] & 0xFFFF0000u);
+#pragma unroll
+                for (int m = 0; m < MAXM; ++m) {
+                    acc[m] = __fmaf_rn(wl, hr[i][m][2 * v], acc[m]);
+                    acc[m] = __fmaf_rn(wh, hr[i][m][2 * v + 1], acc[m]);
+                }
+            }
+        }
+        const int r = row0 + (wv * NR + j) * RPI + rsub;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const float o = row_sum<LPR>(acc[m]);
+            if (m < tk.n && cp == 0 && r < H) a.shared_out[(int64_t)tk.tok[m] * H + r] = o;
+        }
+    }
+}
+
+template <int LPR, int CPL, int SLPR, int SCPL, int MAXM, int NR>
+__global__ __launch_bounds__(256) void k_gemv_down(FfnArgs a, int wgs_per_expert, int n_routed_wgs,
+                                                    const _Float16 *__restrict__ h, const float *__restrict__ hs) {
+    const int bid = blockIdx.x;
+    if (bid < n_routed_wgs) {
+        int e;
+        Tokens<MAXM> tk;
+        if (!routed_tokens<MAXM>(a, bid / wgs_per_expert, e, tk)) return;
+        constexpr int ROWS = WAVES * NR * (64 / LPR);
+        routed_down<LPR, CPL, MAXM, NR>(a, e, tk, (bid % wgs_per_expert) * ROWS, h);
+    } else {
+        Tokens<MAXM> tk;
+        all_tokens<MAXM>(a, tk);
+        constexpr int SNR = shared_nr<SCPL>();
+        constexpr int ROWS = WAVES * SNR * (64 / SLPR);
+        shared_down<SLPR, SCPL, MAXM, SNR>(a, tk, (bid - n_routed_wgs) * ROWS, hs);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+// (lanes per row, chunks per lane) for a row of `len` elements in chunks of `per_chunk`.
+bool split(int len, int per_chunk, int max_cpl, int &lpr, int &cpl) {
+    if (len % per_chunk) return false;
+    const int nch = len / per_chunk;
+    if (nch <= 64) {
+        if (64 % nch) return false;
+        lpr = nch; cpl = 1;
+        return nch >= 2;
+    }
+    if (nch % 64) return false;
+    lpr = 64; cpl = nch / 64;
+    return cpl <= max_cpl;
+}
+
+constexpr int NR = 4;
+
+template <int MAXM, int LPR, int CPL, int SLPR, int SCPL>
+hipError_t run_gateup(const FfnArgs &a, int max_active, _Float16 *h, float *hs, hipStream_t st) {
+    const int rows = WAVES * NR * (64 / LPR);
+    const int wpe = (a.I + rows - 1) / rows;
+    const int nr = max_active * wpe;
+    int ns = 0;
+    if (a.Is > 0) {
+        const int srows = WAVES * shared_nr<SCPL>() * (64 / SLPR);
+        ns = (a.Is + srows - 1) / srows;
+    }
+    hipLaunchKernelGGL((k_gemv_gateup<LPR, CPL, SLPR, SCPL, MAXM, NR>), dim3(nr + ns), dim3(256), 0, st, a, wpe, nr, h,
+                       hs);
+    return hipGetLastError();
+}
+
+template <int MAXM, int LPR, int CPL, int SLPR, int SCPL>
+hipError_t run_down(const FfnArgs &a, int max_active, const _Float16 *h, const float *hs, hipStream_t st) {
+    const int rows = WAVES * NR * (64 / LPR);
+    const int wpe = (a.H + rows - 1) / rows;
+    const int nr = max_active * wpe;
+    int ns = 0;
+    if (a.Is > 0) {
+        const int srows = WAVES * shared_nr<SCPL>() * (64 / SLPR);
+        ns = (a.H + srows - 1) / srows;
+    }
+    hipLaunchKernelGGL((k_gemv_down<LPR, CPL, SLPR, SCPL, MAXM, NR>), dim3(nr + ns), dim3(256), 0, st, a, wpe, nr, h,
+                       hs);
+    return hipGetLastError();
+}
+
+template <int MAXM>
+hipError_t dispatch(const FfnArgs &a, _Float16 *h, float *hs, hipStream_t st) {
+    const int max_active = min(a.T * a.k, a.E);
+    hipError_t e = hipErrorInvalidValue;
+    // gate/up: routed rows of H (64 per chunk), shared rows of H (8 per chunk)
+    if (a.H == 4096) e = run_gateup<MAXM, 64, 1, 64, 8>(a, max_active, h, hs, st);
+    else if (a.H == 2048) e = run_gateup<MAXM, 32, 1, 64, 4>(a, max_active, h, hs, st);
+    else if (a.H == 1024) e = run_gateup<MAXM, 16, 1, 64, 2>(a, max_active, h, hs, st);
+    else if (a.H == 512) e = run_gateup<MAXM, 8, 1, 64, 1>(a, max_active, h, hs, st);
+    if (e != hipSuccess) return e;
+    // down: routed rows of I (64 per chunk), shared rows of Is (8 per chunk)
+    e = hipErrorInvalidValue;
+    const int Is = a.Is > 0 ? a.Is : a.I;
+#define MOE_DOWN(I_, LPR_, SI_, SLPR_, SCPL_)                                                       \
+    if (a.I == I_ && Is == SI_) return run_down<MAXM, LPR_, 1, SLPR_, SCPL_>(a, max_active, h, hs, st);
+    MOE_DOWN(2048, 32, 2048, 64, 4)
+    MOE_DOWN(1024, 16, 1024, 64, 2)
+    MOE_DOWN(512, 8, 512, 64, 1)
+    MOE_DOWN(256, 4, 256, 32, 1)
+    MOE_DOWN(2048, 32, 1024, 64, 2)
+    MOE_DOWN(1024, 16, 2048, 64, 4)
+#undef MOE_DOWN
+    return e;
+}
+
+}  // namespace
+
+namespace moe {
+
+bool ffn_gemv_supported(const FfnArgs &a) {
+    if (!a.x_bf16 || a.fmt_gu != FMT_IQ2X || a.fmt_d != FMT_Q2K || a.T > 4) return false;
+    if (!(a.H == 4096 || a.H == 2048 || a.H == 1024 || a.H == 512)) return false;
+    const int Is = a.Is > 0 ? a.Is : a.I;
+    const int pairs[6][2] = {{2048, 2048}, {1024, 1024}, {512, 512}, {256, 256}, {2048, 1024}, {1024, 2048}};
+    for (auto &p : pairs)
+        if (a.I == p[0] && Is == p[1]) return true;
+    return false;
+}
+
+size_t ffn_workspace_gemv(int H, int I, int E, int k, int Is, int T) {
+    (void)H; (void)E;
+    size_t hb = ((size_t)T * k * I * sizeof(_Float16) + 255) / 256 * 256;
+    return hb + (size_t)T * Is * sizeof(float) + 256;
+}
+
+hipError_t launch_ffn_gemv(const FfnArgs &a, hipStream_t st) {
+    _Float16 *h = static_cast<_Float16 *>(a.ws);
+    size_t hb = ((size_t)a.T * a.k * a.I * sizeof(_Float16) + 255) / 256 * 256;
+    float *hs = reinterpret_cast<float *>(static_cast<char *>(a.ws) + hb);
+    if (a.T == 1) return dispatch<1>(a, h, hs, st);
+    return dispatch<4>(a, h, hs, st);
+}
+
+}  // namespace moe

@@ -1,0 +1,63 @@
+// Internal launch interfaces between the C-ABI host code (api.cpp) and the
+// kernel translation units.  Every launcher enqueues on `st` and returns the
+// launch status; argument checking has already happened in api.cpp.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum { FMT_IQ2X = 1, FMT_Q2K = 2, FMT_Q4K = 3 };
+
+// prep.hip
+hipError_t launch_prepare(int fmt, int64_t NB, const void *canonical, void *prepared, hipStream_t st);
+// Decodes blocks [blk0, blk0 + nblk) of a stack of NB prepared blocks.
+hipError_t launch_dequant(int fmt, int64_t NB, int64_t blk0, int64_t nblk, const void *prepared,
+                          const uint8_t *codebook, float *out, hipStream_t st);
+
+// route.hip
+struct RouteArgs {
+    const void *x;
+    int x_bf16;
+    int T, H;
+    const void *w;
+    int w_bf16;
+    int E;
+    const float *bias;
+    int k;
+    int32_t *topk_idx;
+    float *topk_w;
+    float *logits_out;   // optional
+    int32_t *offsets, *perm, *active;
+    float *logits_ws;    // [T][E] scratch
+};
+hipError_t launch_route(const RouteArgs &a, hipStream_t st);
+
+// ffn_*.hip
+struct FfnArgs {
+    int H, I, E, k, T;
+    int fmt_gu, fmt_d;
+    const uint8_t *gate, *up, *down;   // prepared stacks
+    const uint8_t *codebook;
+    int Is;
+    const uint16_t *sg, *su, *sd;      // bf16
+    const void *x;
+    int x_bf16;
+    const int32_t *topk_idx, *offsets, *perm, *active;
+    float *slot_out, *shared_out;
+    void *ws;
+};
+size_t ffn_workspace_generic(int H, int I, int E, int k, int Is, int T);
+hipError_t launch_ffn_generic(const FfnArgs &a, hipStream_t st);
+size_t ffn_workspace_gemv(int H, int I, int E, int k, int Is, int T);
+bool ffn_gemv_supported(const FfnArgs &a);
+hipError_t launch_ffn_gemv(const FfnArgs &a, hipStream_t st);
+size_t ffn_workspace_gemm(int H, int I, int E, int k, int Is, int T);
+bool ffn_gemm_supported(const FfnArgs &a);
+hipError_t launch_ffn_gemm(const FfnArgs &a, hipStream_t st);
+
+// combine.hip
+hipError_t launch_combine(const float *slot_out, const float *topk_w, const float *shared_out, int T, int k, int H,
+                          float *y, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,191 @@
+/*
+ * moe2bit.h -- C ABI of the routed 2-bit Mixture-of-Experts FFN layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (source pages: "antirez가 만든 DeepSeek V4 Flash 전용 로컬 추론 엔진 ds4",
+ * summary bullets on 2-bit quantization; "antirez/ds4 — Metal용 DeepSeek V4 Flash
+ * 로컬 추론 엔진 완벽 가이드", section on the design philosophy): only the routed
+ * experts are quantized -- up/gate in an IQ2_XXS-style codebook format ("iq2x"),
+ * down in a Q2_K-style super-block format ("q2k"); a 4-bit Q4_K-style variant
+ * ("q4k") exists.  The shared expert and the router stay at full precision.
+ *
+ *   y[t] = sum_{j<k} w[t][j] * FFN_{e[t][j]}(x[t]) + FFN_shared(x[t])
+ *   FFN(x) = Wd (silu(Wg x) * (Wu x))
+ *
+ * and the work is split into three calls, all asynchronous on the caller's
+ * HIP stream:
+ *   moe_route       router logits, top-k + renormalised softmax weights, and
+ *                   the token-to-expert permutation (counts, offsets, order);
+ *   moe_expert_ffn  the routed experts (gate/up + SwiGLU + down, per slot) and
+ *                   the shared expert;
+ *   moe_combine     the top-k weighted sum of the slot outputs plus the shared
+ *                   output.
+ *
+ * Conventions for every function below.
+ *  - Pointers are DEVICE pointers unless the comment says "host".  The caller
+ *    (e.g. PyTorch) allocates and owns all memory: weights, activations,
+ *    outputs and workspaces.  The library allocates no device memory in the
+ *    layer calls and keeps no pointer after a call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work; nothing synchronizes with the host.
+ *  - Every argument is checked on the host before anything is launched.  A
+ *    failed check returns MOE_ERR_INVALID_ARG and launches nothing; a valid but
+ *    unimplemented combination returns MOE_ERR_UNSUPPORTED; a HIP launch error
+ *    returns MOE_ERR_DEVICE.  moe_last_error() describes the last failure on
+ *    the calling thread.  Faults inside kernels surface at the caller's next
+ *    synchronization.  No C++ exception crosses this interface.
+ *  - Non-finite inputs are outside the contract.
+ *
+ * Canonical block formats (256 weights per block; blocks run along the
+ * flattened row-major [out][in] matrix; little-endian):
+ *   iq2x  66 B: fp16 d | 8 x { idx[4] (codebook row per 8 weights),
+ *               u32 aux: bits 7j..7j+6 = signs of weights 8j..8j+6 (set =
+ *               negative), the 8th sign makes the count of negatives even,
+ *               bits 28..31 = group scale s } ;  w = d * (2s+1) * C[idx][i] * sign
+ *   q2k   84 B: fp16 d | fp16 dmin | 16 x (sc | m << 4) per 16 weights |
+ *               64 B of 2-bit q (weight n: byte n/4, bits 2(n%4)) ;
+ *               w = d * sc * q - dmin * m
+ *   q4k  144 B: fp16 d | fp16 dmin | 12 B = sixteen 6-bit fields (sc0..sc7,
+ *               m0..m7; field f at bits 6f) | 128 B of 4-bit q (weight n: byte
+ *               n/2, low nibble when n even) ; w = d * sc * q - dmin * m
+ * The codebook C is 256 x 8 magnitudes; its entries must be 1, 2 or 3.
+ * These layouts are this library's reading of the format names on the pages.
+ */
+#ifndef MOE2BIT_H
+#define MOE2BIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_DEVICE = 3
+} moe_status;
+
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
+
+typedef enum { MOE_FMT_IQ2X = 1, MOE_FMT_Q2K = 2, MOE_FMT_Q4K = 3 } moe_format;
+
+/* Expert-FFN kernel family; AUTO picks by token count and shapes. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GENERIC = 1, MOE_PATH_GEMV = 2, MOE_PATH_GEMM = 3 } moe_path;
+
+/*
+ * Description of one layer (host struct; read during the call only).
+ *   hidden (H), inter (I), n_experts (E), top_k (k): 1 <= k <= E <= 256.
+ *   gate, up: E stacked [I][H] matrices, down: E stacked [H][I] matrices, each
+ *     in the PREPARED layout written by moe_prepare_weights (same byte count
+ *     as the canonical blocks).  gate_up_fmt is iq2x or q4k; down_fmt is q2k
+ *     or q4k.
+ *   codebook: device, 256 x 8 uint8 magnitudes in {1, 2, 3} (iq2x only).
+ *   shared_inter (Is): 0 = no shared expert; else shared_gate, shared_up
+ *     [Is][H] and shared_down [H][Is], bf16 row-major.
+ *   path: kernel family for moe_expert_ffn (MOE_PATH_AUTO normally).
+ */
+typedef struct {
+    int32_t hidden, inter, n_experts, top_k;
+    int32_t gate_up_fmt, down_fmt;
+    const void *gate, *up, *down;
+    const uint8_t *codebook;
+    int32_t shared_inter;
+    const void *shared_gate, *shared_up, *shared_down;
+    int32_t path;
+} moe_layer_desc;
+
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+/* Text for the last failure on the calling thread ("" if none). Host string,
+ * owned by the library, valid until the next call on this thread. */
+const char *moe_last_error(void);
+
+/* Bytes of n_mats stacked [rows][cols] matrices in format fmt (canonical and
+ * prepared layouts have the same size).  0 if the shape is not a whole number
+ * of blocks or the format is unknown. */
+size_t moe_weight_bytes(int32_t fmt, int64_t n_mats, int64_t rows, int64_t cols);
+
+/*
+ * Repack n_mats stacked [rows][cols] matrices from the canonical block layout
+ * (`canonical`, device) into the device layout the kernels read (`prepared`,
+ * device, moe_weight_bytes(...) bytes, 16-byte aligned, must not overlap
+ * `canonical`).  rows*cols must be a multiple of 256, and sub-blocks may not
+ * straddle rows: cols % 32 == 0 (iq2x, q4k) or cols % 16 == 0 (q2k).
+ * Offline step (weight load), not part of the per-token path.
+ */
+moe_status moe_prepare_weights(int32_t fmt, int64_t n_mats, int64_t rows, int64_t cols, const void *canonical,
+                               void *prepared, void *stream);
+
+/*
+ * Decode prepared weights to fp32 (parity/debug export).  `prepared` holds
+ * n_mats stacked [rows][cols] matrices; matrices mat_begin .. mat_begin +
+ * mat_count - 1 are written to out[mat_count*rows*cols] in row-major order,
+ * every value exact.  codebook as in moe_layer_desc (iq2x only, else may be
+ * NULL).
+ */
+moe_status moe_dequantize(int32_t fmt, const void *prepared, int64_t n_mats, int64_t rows, int64_t cols,
+                          int64_t mat_begin, int64_t mat_count, const uint8_t *codebook, float *out, void *stream);
+
+/* Workspace bytes moe_route needs for n_tokens tokens. */
+size_t moe_route_workspace(int32_t n_tokens, int32_t n_experts, int32_t top_k);
+
+/*
+ * Routing for T tokens.
+ *   x [T][H] (x_dt), w_router [E][H] (w_dt), bias [E] fp32 or NULL.
+ *   logit[t][e] = fp32( sum_h w[e][h] * x[t][h] ) (+ bias[e], added in fp64 to
+ *     the fp32 logit and rounded to fp32), where the sum takes exact products
+ *     in binary64 in a fixed order: 64 partials, partial p holding h = p, p+64,
+ *     ... in increasing h, then p[i] += p[i+s] for s = 32, 16, ..., 1.
+ *   topk_idx [T][k] int32: experts ordered by (descending logit, ascending
+ *     index); topk_w [T][k] fp32: softmax over the selected logits (binary64,
+ *     rounded to fp32).
+ *   logits [T][E] fp32 or NULL (optional copy of the logits).
+ *   expert_offsets [E+1], perm [T*k], active [1+E] (int32): slot s = t*k + j
+ *     carries expert topk_idx[t][j]; perm lists the slots grouped by expert in
+ *     ascending expert order, in slot order within an expert (stable);
+ *     expert_offsets is the exclusive scan of the per-expert counts;
+ *     active[0] = number of experts with a slot, then those experts ascending.
+ *   ws: workspace of at least moe_route_workspace(T, E, k) bytes.
+ * Requires 1 <= T, H % 64 == 0, 1 <= k <= E <= 256.
+ */
+moe_status moe_route(const void *x, int32_t x_dt, int32_t n_tokens, int32_t hidden, const void *w_router,
+                     int32_t w_dt, int32_t n_experts, const float *bias, int32_t top_k, int32_t *topk_idx,
+                     float *topk_w, float *logits, int32_t *expert_offsets, int32_t *perm, int32_t *active, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* Workspace bytes moe_expert_ffn needs for n_tokens tokens of layer L. */
+size_t moe_expert_ffn_workspace(const moe_layer_desc *L, int32_t n_tokens);
+
+/*
+ * Routed and shared experts for T tokens.
+ *   x [T][H] (x_dt; fp32 activations take the generic kernels).
+ *   topk_idx, expert_offsets, perm, active: as written by moe_route.
+ *   slot_out [T*k][H] fp32: slot s = t*k + j gets FFN_{topk_idx[t][j]}(x[t]).
+ *   shared_out [T][H] fp32: FFN_shared(x[t]); NULL iff L->shared_inter == 0.
+ *   ws: workspace of at least moe_expert_ffn_workspace(L, T) bytes.
+ * Numerics: decoded weights are exact; products accumulate in fp32.  The
+ * SwiGLU output h is kept in fp32 (decode/generic kernels) or in fp16 (grouped
+ * GEMM kernels, T > 4).
+ */
+moe_status moe_expert_ffn(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
+                          const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
+                          const int32_t *active, float *slot_out, float *shared_out, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/*
+ * y[t][c] = sum_{j<k} topk_w[t][j] * slot_out[t*k+j][c] (+ shared_out[t][c]),
+ * j in increasing order, fp32.  shared_out may be NULL.
+ */
+moe_status moe_combine(const float *slot_out, const float *topk_w, const float *shared_out, int32_t n_tokens,
+                       int32_t top_k, int32_t hidden, float *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE2BIT_H */

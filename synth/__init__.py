@@ -182,6 +182,19 @@ def activations(name: str, n_tokens: int, hidden: int, bf16: bool, seed: Optiona
     return to_bf16_bits(x) if bf16 else x
 
 
+def make_router(spec: LayerSpec | str):
+    """(w_router, bias) of a layer without its experts (same draws as make_layer)."""
+    if isinstance(spec, str):
+        spec = SPECS[spec]
+    s = spec.layer_seed
+    wr = normal_f32(s, _T_ROUTER, (spec.n_experts, spec.hidden), 0.02)
+    wr = to_bf16_bits(wr) if spec.x_bf16 else wr
+    bias = None
+    if spec.bias_std > 0:
+        bias = normal_f32(BIAS_SEEDS.get(spec.name, s + 7), _T_BIAS, (spec.n_experts,), spec.bias_std)
+    return wr, bias
+
+
 def make_layer(spec: LayerSpec | str, quantizer: Optional[Callable] = None, keep_masters: bool = False) -> Layer:
     """Build a seeded layer.
 
@@ -193,11 +206,7 @@ def make_layer(spec: LayerSpec | str, quantizer: Optional[Callable] = None, keep
     H, I, E = spec.hidden, spec.inter, spec.n_experts
     s = spec.layer_seed
     cb = codebook(0)
-    wr = normal_f32(s, _T_ROUTER, (E, H), 0.02)
-    wr = to_bf16_bits(wr) if spec.x_bf16 else wr
-    bias = None
-    if spec.bias_std > 0:
-        bias = normal_f32(BIAS_SEEDS.get(spec.name, s + 7), _T_BIAS, (E,), spec.bias_std)
+    wr, bias = make_router(spec)
     masters = {}
     if quantizer is not None:
         blocks = {}

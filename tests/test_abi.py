@@ -1,0 +1,134 @@
+"""Host-only checks of the C-ABI library (no GPU needed): it loads, exports
+every function include/moe2bit.h declares, reports its ABI version, and
+rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "bit_quantized_moe_permute_amd", "libmoe2bit.so")
+HDR = os.path.join(ROOT, "include", "moe2bit.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmoe2bit.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    L = ctypes.CDLL(LIB)
+    return L
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moe2bit.h but not exported"
+
+
+def test_binding_lists_the_same_symbols():
+    src = open(os.path.join(ROOT, "bit_quantized_moe_permute_amd", "__init__.py")).read()
+    exported = re.search(r"EXPORTS = \[(.*?)\]", src, re.S).group(1)
+    assert sorted(re.findall(r'"(moe_\w+)"', exported)) == declared_functions()
+
+
+def test_abi_version(lib):
+    lib.moe_abi_version.restype = ctypes.c_int
+    hdr = open(HDR).read()
+    assert lib.moe_abi_version() == int(re.search(r"#define MOE_ABI_VERSION (\d+)", hdr).group(1))
+
+
+def test_weight_bytes(lib):
+    f = lib.moe_weight_bytes
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+    assert f(1, 256, 2048, 4096) == 256 * 2048 * 16 * 66
+    assert f(2, 256, 4096, 2048) == 256 * 4096 * 8 * 84
+    assert f(3, 2, 256, 256) == 2 * 256 * 144
+    assert f(2, 8, 256, 128) == 8 * 128 * 84          # blocks span two rows
+    assert f(9, 1, 256, 256) == 0 and f(1, 1, 3, 5) == 0
+
+
+def _err(lib):
+    lib.moe_last_error.restype = ctypes.c_char_p
+    return lib.moe_last_error().decode()
+
+
+def test_route_rejects_bad_arguments(lib):
+    f = lib.moe_route
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    f.restype = ctypes.c_int
+    f.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    p = vp(0x1000)
+    ws = 1 << 20
+    # null x
+    assert f(None, 1, 4, 4096, p, 1, 256, None, 8, p, p, None, p, p, p, p, ws, None) == 1
+    assert "null" in _err(lib)
+    # top_k > E
+    assert f(p, 1, 4, 4096, p, 1, 8, None, 9, p, p, None, p, p, p, p, ws, None) == 1
+    # E > 256
+    assert f(p, 1, 4, 4096, p, 1, 300, None, 8, p, p, None, p, p, p, p, ws, None) == 1
+    # hidden not a multiple of 64
+    assert f(p, 1, 4, 100, p, 1, 8, None, 2, p, p, None, p, p, p, p, ws, None) == 1
+    # workspace too small
+    assert f(p, 1, 4, 4096, p, 1, 256, None, 8, p, p, None, p, p, p, p, 16, None) == 1
+    assert "workspace" in _err(lib)
+    # unknown dtype
+    assert f(p, 7, 4, 4096, p, 1, 256, None, 8, p, p, None, p, p, p, p, ws, None) == 1
+
+
+def test_expert_ffn_rejects_bad_layers(lib):
+    import bit_quantized_moe_permute_amd as m  # noqa: F401  (loads; host only)
+    from bit_quantized_moe_permute_amd import LayerDesc
+    f = lib.moe_expert_ffn
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    p = vp(0x1000)
+    d = LayerDesc(hidden=4096, inter=2048, n_experts=256, top_k=8, gate_up_fmt=1, down_fmt=2, gate=0x1000, up=0x1000,
+                  down=0x1000, codebook=0x1000, shared_inter=0, path=0)
+    # x dtype unknown
+    assert f(ctypes.byref(d), p, 5, 1, p, p, p, p, p, None, p, 1 << 30, None) == 1
+    # shared_out given without a shared expert
+    assert f(ctypes.byref(d), p, 1, 1, p, p, p, p, p, p, p, 1 << 30, None) == 1
+    # bad format
+    d.gate_up_fmt = 2
+    assert f(ctypes.byref(d), p, 1, 1, p, p, p, p, p, None, p, 1 << 30, None) == 1
+    assert "format" in _err(lib)
+    d.gate_up_fmt = 1
+    # misaligned weights
+    d.gate = 0x1004
+    assert f(ctypes.byref(d), p, 1, 1, p, p, p, p, p, None, p, 1 << 30, None) == 1
+    d.gate = 0x1000
+    # top_k > E
+    d.top_k = 300
+    assert f(ctypes.byref(d), p, 1, 1, p, p, p, p, p, None, p, 1 << 30, None) == 1
+    d.top_k = 8
+    # workspace too small
+    assert f(ctypes.byref(d), p, 1, 1, p, p, p, p, p, None, p, 8, None) == 1
+    assert "workspace" in _err(lib)
+    # fp32 activations cannot take the decode path when it is forced
+    d.path = 2
+    assert f(ctypes.byref(d), p, 0, 1, p, p, p, p, p, None, p, 1 << 30, None) == 2
+
+
+def test_prepare_and_combine_reject_bad_arguments(lib):
+    vp = ctypes.c_void_p
+    f = lib.moe_prepare_weights
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
+    assert f(1, 1, 256, 100, vp(0x1000), vp(0x100000), None) == 1      # cols % 32
+    assert f(1, 1, 256, 256, vp(0x1000), vp(0x1008), None) == 1         # overlap / misaligned
+    assert f(5, 1, 256, 256, vp(0x1000), vp(0x100000), None) == 1       # format
+    g = lib.moe_combine
+    g.restype = ctypes.c_int
+    g.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]
+    assert g(None, vp(0x1000), None, 1, 8, 4096, vp(0x1000), None) == 1
+    assert g(vp(0x1000), vp(0x1000), None, 0, 8, 4096, vp(0x1000), None) == 1

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: dequantized weights, logits, routing indices, offsets, permutation and
+active lists bit-exact; routing weights within 1e-6; slot, shared and layer
+outputs within a per-token relative L2 error of 1e-3 (the layer's stated
+tolerance with fp32 accumulation).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+def note(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import bit_quantized_moe_permute_amd as m
+    return m
+
+
+def dev_x(x: np.ndarray) -> torch.Tensor:
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def rel_l2_rows(got: np.ndarray, want: np.ndarray) -> np.ndarray:
+    got = got.reshape(want.shape[0], -1).astype(np.float64)
+    want = want.reshape(want.shape[0], -1)
+    den = np.linalg.norm(want, axis=1)
+    return np.linalg.norm(got - want, axis=1) / np.where(den > 0, den, 1.0)
+
+
+# ----------------------------------------------------------------------------
+# formats
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", [oracle.FMT_IQ2X, oracle.FMT_Q2K, oracle.FMT_Q4K])
+@pytest.mark.parametrize("kind", ["quantized", "random"])
+def test_dequant_bit_exact(m, fmt, kind):
+    note(f"dequant fmt={fmt} kind={kind}")
+    cb = synth.codebook()
+    if kind == "quantized":
+        w = synth.normal_f32(3, 50, (6, 96, 256), 0.02)         # 6 matrices [96][256]
+        blocks = oracle.quantize(fmt, w.reshape(-1), cb)
+    else:
+        blocks = synth.random_blocks(fmt, 6 * 96, 4, 51)
+    n_mats, rows, cols = 6, 96, 256
+    canon = torch.from_numpy(blocks).cuda()
+    prep = torch.empty_like(canon)
+    m.moe_prepare_weights(fmt, n_mats, rows, cols, canon, prep)
+    dcb = torch.from_numpy(cb.reshape(-1)).cuda()
+    want = oracle.dequantize(fmt, blocks, cb).reshape(n_mats, rows, cols)
+    out = torch.empty(n_mats, rows, cols, dtype=torch.float32, device="cuda")
+    m.moe_dequantize(fmt, prep, n_mats, rows, cols, 0, n_mats, dcb, out)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+    # a sub-range of matrices
+    out2 = torch.empty(2, rows, cols, dtype=torch.float32, device="cuda")
+    m.moe_dequantize(fmt, prep, n_mats, rows, cols, 3, 2, dcb, out2)
+    assert np.array_equal(out2.cpu().numpy().astype(np.float64), want[3:5])
+
+
+def test_dequant_rows_shorter_than_a_block(m):
+    """The tiny layer's down matrices are [256][128] q2k: blocks span two rows."""
+    note("dequant tiny down")
+    L = synth.make_layer("tiny", quantizer=oracle.quantize)
+    canon = torch.from_numpy(L.down).cuda()
+    prep = torch.empty_like(canon)
+    m.moe_prepare_weights(oracle.FMT_Q2K, 8, 256, 128, canon, prep)
+    out = torch.empty(8, 256, 128, dtype=torch.float32, device="cuda")
+    m.moe_dequantize(oracle.FMT_Q2K, prep, 8, 256, 128, 0, 8, None, out)
+    assert np.array_equal(out.cpu().numpy().astype(np.float64).reshape(-1), oracle.dequantize(oracle.FMT_Q2K, L.down))
+
+
+# ----------------------------------------------------------------------------
+# routing
+# ----------------------------------------------------------------------------
+def _route_gpu(m, x, w_router, E, k, bias=None):
+    T = x.shape[0]
+    xd = dev_x(x)
+    wd = dev_x(w_router)
+    bd = None if bias is None else torch.from_numpy(bias).cuda()
+    i32 = dict(dtype=torch.int32, device="cuda")
+    idx = torch.empty(T, k, **i32)
+    tw = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    lg = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    off = torch.empty(E + 1, **i32)
+    perm = torch.empty(T * k, **i32)
+    act = torch.full((E + 1,), -7, **i32)
+    ws = torch.empty(max(m.moe_route_workspace(T, E, k), 256), dtype=torch.uint8, device="cuda")
+    m.moe_route(xd, wd, E, k, idx, tw, off, perm, act, ws, bias=bd, logits=lg)
+    torch.cuda.synchronize()
+    return lg.cpu().numpy(), idx.cpu().numpy(), tw.cpu().numpy(), off.cpu().numpy(), perm.cpu().numpy(), act.cpu().numpy()
+
+
+def _check_route(m, x, w_router, E, k, bias=None):
+    lg, idx, tw, off, perm, act = _route_gpu(m, x, w_router, E, k, bias)
+    ol, oi, ow = oracle.route(x, w_router, k, bias)
+    assert np.array_equal(lg.view(np.uint32), ol.view(np.uint32)), np.argwhere(lg != ol)[:5]
+    assert np.array_equal(idx, oi)
+    assert np.abs(tw.astype(np.float64) - ow).max() <= 1e-6
+    oo, op, oa = oracle.permute(oi, E)
+    assert np.array_equal(off, oo)
+    assert np.array_equal(perm, op)
+    assert np.array_equal(act[: oa[0] + 1], oa[: oa[0] + 1])
+
+
+ROUTE_CASES = [
+    ("tiny", 4), ("small", 1), ("small", 3), ("small", 37), ("mid", 70), ("decode", 1), ("decode", 3),
+    ("decode", 64), ("prefill", 512), ("long", 2048), ("long", 2500),
+]
+
+
+@pytest.mark.parametrize("name,T", ROUTE_CASES, ids=[f"{a}-{b}" for a, b in ROUTE_CASES])
+def test_route_matches_oracle(m, name, T):
+    note(f"route {name} T={T}")
+    sp = synth.SPECS[name]
+    wr, bias = synth.make_router(sp)
+    x = synth.activations(name, T, sp.hidden, sp.x_bf16)
+    _check_route(m, x, wr, sp.n_experts, sp.top_k, bias)
+
+
+@pytest.mark.parametrize("k", [1, 16])
+def test_route_k_extremes(m, k):
+    note(f"route k={k}")
+    wr, _ = synth.make_router("small")
+    x = synth.activations("small", 9, 512, True)
+    _check_route(m, x, wr, 16, k)
+
+
+def test_route_zero_input_ties(m):
+    note("route zero input")
+    wr, _ = synth.make_router("small")
+    x = np.zeros((5, 512), np.uint16)
+    _, idx, tw, _, _, _ = _route_gpu(m, x, wr, 16, 4)
+    assert np.array_equal(idx, np.tile(np.arange(4), (5, 1)))
+    assert np.array_equal(tw, np.full((5, 4), 0.25, np.float32))
+
+
+def test_route_summation_order_golden(m):
+    """tests/golden/router_order.txt: cancellation cases where the fixed order decides the logit."""
+    from test_oracle_layer import _router_order_cases
+    for name, H, entries, want in _router_order_cases():
+        note(f"route order {name}")
+        x = np.ones((1, H), np.float32)
+        w = np.zeros((2, H), np.float32)
+        for h, v in entries:
+            w[0, h] = v
+        lg, _, _, _, _, _ = _route_gpu(m, x, w, 2, 1)
+        assert lg[0, 0] == np.float32(want), (name, lg[0, 0])
+
+
+# ----------------------------------------------------------------------------
+# layer
+# ----------------------------------------------------------------------------
+_LAYERS = {}
+
+
+def _layer(name):
+    if name not in _LAYERS:
+        sp = synth.SPECS[name]
+        _LAYERS[name] = synth.make_layer(sp) if sp.hidden >= 4096 else synth.make_layer(sp, quantizer=oracle.quantize)
+    return _LAYERS[name]
+
+
+_DEV = {}
+
+
+def _run_layer(m, L, x, path):
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward
+    key = (L.spec.name, path)
+    if key not in _DEV:
+        if len(_DEV) > 3:
+            _DEV.clear()
+        _DEV[key] = DeviceLayer.from_synth(L, path=path)
+    DL = _DEV[key]
+    b = LayerBuffers.allocate(DL, x.shape[0])
+    forward(DL, dev_x(x), b)
+    torch.cuda.synchronize()
+    return {k: (None if v is None else v.cpu().numpy()) for k, v in
+            dict(y=b.y, slot_out=b.slot_out, shared_out=b.shared_out, topk_idx=b.topk_idx).items()}
+
+
+def _oracle_layer(L, x):
+    sp = L.spec
+    return oracle.layer(x, L.w_router, sp.top_k, sp.n_experts, sp.inter, sp.gate_up_fmt, L.gate, L.up, sp.down_fmt,
+                        L.down, L.codebook, bias=L.bias, shared=L.shared)
+
+
+LAYER_CASES = [
+    ("tiny", 4, 0), ("small", 1, 0), ("small", 3, 0), ("small", 4, 0), ("small", 1, 1), ("small", 37, 1),
+    ("mid", 2, 0), ("mid", 9, 1), ("mid_fp32", 3, 0),
+]
+
+
+@pytest.mark.parametrize("name,T,path", LAYER_CASES, ids=[f"{a}-T{b}-p{c}" for a, b, c in LAYER_CASES])
+def test_layer_matches_oracle(m, name, T, path):
+    note(f"layer {name} T={T} path={path}")
+    L = _layer(name)
+    sp = L.spec
+    x = synth.activations(name, T, sp.hidden, sp.x_bf16)
+    got = _run_layer(m, L, x, path)
+    ref = _oracle_layer(L, x)
+    assert np.array_equal(got["topk_idx"], ref["topk_idx"])
+    assert rel_l2_rows(got["slot_out"], ref["slot_out"]).max() <= TOL
+    if ref["shared_out"] is not None:
+        assert rel_l2_rows(got["shared_out"], ref["shared_out"]).max() <= TOL
+    err = rel_l2_rows(got["y"], ref["y"])
+    note(f"  max per-token rel L2 = {err.max():.3e}")
+    assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_decode_layer_full_size(m, T):
+    """Full-size decode layer (hidden 4096, 256 experts, top-8, intermediate
+    2048, bf16 shared expert) on several independent calls."""
+    L = _layer("decode")
+    sp = L.spec
+    xs = synth.activations("decode", 4 * T, sp.hidden, True, seed=901 + T)
+    for c in range(4):
+        note(f"decode full size T={T} call {c}")
+        x = xs[c * T:(c + 1) * T]
+        got = _run_layer(m, L, x, 0)
+        ref = _oracle_layer(L, x)
+        assert np.array_equal(got["topk_idx"], ref["topk_idx"])
+        err = rel_l2_rows(got["y"], ref["y"])
+        note(f"  max per-token rel L2 = {err.max():.3e}")
+        assert err.max() <= TOL
+
+
+def test_combine_matches_numpy(m):
+    note("combine")
+    g = np.random.default_rng(0)
+    for T, k, H, shared in ((1, 8, 4096, True), (7, 3, 100, False), (5, 2, 256, True)):
+        o = g.standard_normal((T * k, H)).astype(np.float32)
+        w = g.random((T, k)).astype(np.float32)
+        s = g.standard_normal((T, H)).astype(np.float32) if shared else None
+        y = torch.empty(T, H, dtype=torch.float32, device="cuda")
+        m.moe_combine(torch.from_numpy(o).cuda(), torch.from_numpy(w).cuda(),
+                      None if s is None else torch.from_numpy(s).cuda(), T, k, H, y)
+        want = oracle.combine(o.astype(np.float64), w.astype(np.float64), None if s is None else s.astype(np.float64))
+        assert rel_l2_rows(y.cpu().numpy(), want).max() <= 1e-6
