@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed 2-bit MoE FFN layer on one MI355X.
+
+A step is one pass of the whole layer (route -> permute -> routed experts +
+shared expert -> combine) over one batch of synthetic input.  The default
+workload is decode at batch 1: hidden 4096, 256 routed experts, top-8,
+intermediate 2048, one bf16 shared expert (intermediate 2048), bf16
+activations, 1000 seeded tokens, one token per step.  Each token runs on one of
+several device copies of the layer (cycled), so consecutive tokens cannot
+reuse each other's weights from the 256 MB last-level cache; a real model's
+consecutive tokens through one layer are separated by all its other layers.
+
+Prints ONE JSON line (rank 0).  Timed region: exactly --steps steps,
+captured once in a HIP graph and replayed, bracketed by device
+synchronizations; inputs and weights are resident in HBM before it starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "routed-MoE layer tokens/sec at decode B=1 and prefill; % of HBM/MFMA peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--layers", type=int, default=6, help="device copies of the layer, cycled per token")
+    p.add_argument("--kernel-reps", type=int, default=0, help="launches per kernel timing pass (default: steps)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def decode_bytes(H, I, E, k, Is):
+    """Algorithmic bytes per decode token, per launch family (selected experts only)."""
+    iq2x = I * H // 256 * 66
+    q2k = H * I // 256 * 84
+    gate_up = k * 2 * iq2x + 2 * Is * H * 2 + H * 2 + (k * I * 2 + Is * 4)          # weights, x, h out
+    down = k * q2k + H * Is * 2 + (k * I * 2 + Is * 4) + (k * H * 4 + H * 4)         # weights, h in, outputs
+    route = E * H * 2 + H * 2
+    combine = k * H * 4 + H * 4 + H * 4 + k * 4
+    return dict(gate_up=gate_up, down=down, route=route, combine=combine,
+                total=gate_up + down + route + combine)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the layer is a single-GPU hot path "
+                                   "(multi-GPU expert parallelism is described, not built)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from bit_quantized_moe_permute_amd import moe_expert_gate_up, moe_route
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sp = synth.SPECS["decode"]
+    H, I, E, k, Is = sp.hidden, sp.inter, sp.n_experts, sp.top_k, sp.shared_inter
+    K, W = args.steps, args.warmup
+    n_tok = synth.TOKENS["decode"]
+
+    log("generating the decode layer (seeded random blocks)")
+    t0 = time.time()
+    L = synth.make_layer(sp)
+    x_np = synth.activations("decode", n_tok, H, True)
+    layers = [DeviceLayer.from_synth(L, device=dev)]
+    for _ in range(args.layers - 1):
+        layers.append(layers[0].clone())
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    torch.cuda.synchronize()
+    log(f"layer ready in {time.time() - t0:.1f}s ({args.layers} device copies)")
+
+    bufs = [LayerBuffers.allocate(layers[0], 1) for _ in range(2)]
+
+    def step(i):
+        forward(layers[i % args.layers], x[i % n_tok: i % n_tok + 1], bufs[i % 2])
+
+    log(f"warmup {W} steps (eager)")
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    # capture exactly K steps in one graph
+    log(f"capturing {K} steps in a HIP graph")
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(K):
+                step(i)
+    torch.cuda.synchronize()
+    g.replay()                                   # one untimed replay
+    torch.cuda.synchronize()
+    y_graph = bufs[(K - 1) % 2].y.clone()
+    step(K - 1)                                  # eager recomputation of the last step
+    torch.cuda.synchronize()
+    if not torch.equal(y_graph, bufs[(K - 1) % 2].y):
+        raise RuntimeError("graph replay and eager run disagree")
+
+    log("timed region")
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / K
+    value = K / wall
+    log(f"{K} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms -> {value:.0f} tokens/s")
+
+    # dominant kernel: gate/up (+SwiGLU) GEMV, routed and shared rows in one launch
+    reps = args.kernel_reps or K
+    log(f"timing the gate/up kernel over {reps} launches")
+    rb = [LayerBuffers.allocate(layers[0], 1) for _ in range(2)]
+    # per-token routing results, computed once (untimed)
+    ridx = torch.empty(reps, k, dtype=torch.int32, device=dev)
+    roff = torch.empty(reps, E + 1, dtype=torch.int32, device=dev)
+    rperm = torch.empty(reps, k, dtype=torch.int32, device=dev)
+    ract = torch.empty(reps, E + 1, dtype=torch.int32, device=dev)
+    rw = torch.empty(reps, k, dtype=torch.float32, device=dev)
+    b0 = rb[0]
+    for i in range(reps):
+        Li = layers[i % args.layers]
+        moe_route(x[i % n_tok: i % n_tok + 1], Li.w_router, E, k, ridx[i], rw[i], roff[i], rperm[i], ract[i],
+                  b0.ws_route, bias=Li.bias)
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g2, stream=cap):
+            for i in range(reps):
+                Li = layers[i % args.layers]
+                moe_expert_gate_up(Li.desc, x[i % n_tok: i % n_tok + 1], ridx[i], roff[i], rperm[i], ract[i],
+                                   rb[i % 2].ws_ffn)
+    torch.cuda.synchronize()
+    g2.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g2.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    gu_us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = decode_bytes(H, I, E, k, Is)
+    achieved = nbytes["gate_up"] / (gu_us * 1e-6) / 1e9
+    log(f"gate/up kernel: {gu_us:.2f} us/launch, {achieved:.0f} GB/s algorithmic")
+
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "k_gemv_gateup (routed iq2x gate/up + bf16 shared gate/up, fused SwiGLU)",
+                "bytes_per_launch": nbytes["gate_up"], "avg_launch_us": round(gu_us, 3)}
+    step_bw = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(L, x_np, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode B=1: hidden 4096, 256 routed experts top-8, intermediate 2048 "
+                               "(gate/up iq2x 2.06 bpw, down q2k 2.63 bpw), bf16 shared expert 2048, bf16 router; "
+                               f"1000 seeded tokens one per step over {args.layers} cycled layer copies",
+                   "global_batch": 1, "seq_len": 1, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "step": {"bytes_per_token": nbytes["total"], "effective_GBps": round(step_bw, 1),
+                 "hbm_frac": round(step_bw / HBM_PEAK_GBS, 4), "graph_gpu_ms": round(gpu_ms, 3)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(L, x_np, budget_s):
+    """The oracle (binary64, plain C with OpenMP over rows) on a bounded sample of
+    decode tokens, one call per token, until the time budget is spent."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    sp = L.spec
+    done, t0 = 0, time.perf_counter()
+    while True:
+        xt = x_np[done: done + 1]
+        oracle.layer(xt, L.w_router, sp.top_k, sp.n_experts, sp.inter, sp.gate_up_fmt, L.gate, L.up, sp.down_fmt,
+                     L.down, L.codebook, bias=L.bias, shared=L.shared)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= 200:
+            break
+    log(f"oracle: {done} tokens in {el:.1f}s")
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {done} of the 1000 decode tokens, whole layer (route, permute, 8 routed experts, "
+                      f"shared expert, combine) in binary64, {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -23,7 +23,8 @@ ABI_VERSION = 1
 
 EXPORTS = [
     "moe_abi_version", "moe_last_error", "moe_weight_bytes", "moe_prepare_weights", "moe_dequantize",
-    "moe_route_workspace", "moe_route", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_combine",
+    "moe_route_workspace", "moe_route", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_expert_gate_up",
+    "moe_expert_down", "moe_combine",
 ]
 
 
@@ -70,6 +71,10 @@ def _load():
     L.moe_expert_ffn_workspace.argtypes = [ctypes.POINTER(LayerDesc), i32]
     L.moe_expert_ffn.restype = ctypes.c_int
     L.moe_expert_ffn.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_gate_up.restype = ctypes.c_int
+    L.moe_expert_gate_up.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_down.restype = ctypes.c_int
+    L.moe_expert_down.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_combine.restype = ctypes.c_int
     L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
     if L.moe_abi_version() != ABI_VERSION:
@@ -150,6 +155,18 @@ def moe_expert_ffn(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, s
     _check(lib.moe_expert_ffn(ctypes.byref(desc), _ptr(x), _dt(x), T, _ptr(topk_idx), _ptr(expert_offsets),
                               _ptr(perm), _ptr(active), _ptr(slot_out), _ptr(shared_out), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_expert_gate_up(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, ws, stream=None):
+    _check(lib.moe_expert_gate_up(ctypes.byref(desc), _ptr(x), _dt(x), x.shape[0], _ptr(topk_idx),
+                                  _ptr(expert_offsets), _ptr(perm), _ptr(active), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_expert_down(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, slot_out, shared_out, ws, stream=None):
+    _check(lib.moe_expert_down(ctypes.byref(desc), _ptr(x), _dt(x), x.shape[0], _ptr(topk_idx),
+                               _ptr(expert_offsets), _ptr(perm), _ptr(active), _ptr(slot_out), _ptr(shared_out),
+                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_combine(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, y, stream=None):

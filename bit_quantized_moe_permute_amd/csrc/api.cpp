@@ -205,38 +205,62 @@ size_t moe_expert_ffn_workspace(const moe_layer_desc *L, int32_t n_tokens) {
     return m;
 }
 
-moe_status moe_expert_ffn(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
-                          const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
-                          const int32_t *active, float *slot_out, float *shared_out, void *ws, size_t ws_bytes,
-                          void *stream) {
-    moe_status st = check_layer(L, "moe_expert_ffn");
+static moe_status expert_call(const char *fn, int stages, const moe_layer_desc *L, const void *x, int32_t x_dt,
+                              int32_t n_tokens, const int32_t *topk_idx, const int32_t *expert_offsets,
+                              const int32_t *perm, const int32_t *active, float *slot_out, float *shared_out,
+                              void *ws, size_t ws_bytes, void *stream) {
+    moe_status st = check_layer(L, fn);
     if (st != MOE_OK) return st;
-    if (!x || !topk_idx || !expert_offsets || !perm || !active || !slot_out || !ws)
-        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: null pointer");
-    if (x_dt != MOE_DT_F32 && x_dt != MOE_DT_BF16) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: unknown dtype");
-    if (n_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: n_tokens < 1");
-    if ((L->shared_inter > 0) != (shared_out != nullptr))
-        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: shared_out must be given iff the layer has a shared expert");
-    if (!aligned(x, 16) || !aligned(slot_out, 16) || !aligned(ws, 256) || (shared_out && !aligned(shared_out, 16)))
-        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: misaligned pointer (x/outputs 16 B, ws 256 B)");
+    if (!x || !topk_idx || !expert_offsets || !perm || !active || !ws)
+        return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if ((stages & moe::STAGE_DOWN) && !slot_out) return fail(MOE_ERR_INVALID_ARG, "%s: null slot_out", fn);
+    if (x_dt != MOE_DT_F32 && x_dt != MOE_DT_BF16) return fail(MOE_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+    if (n_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "%s: n_tokens < 1", fn);
+    if ((stages & moe::STAGE_DOWN) && (L->shared_inter > 0) != (shared_out != nullptr))
+        return fail(MOE_ERR_INVALID_ARG, "%s: shared_out must be given iff the layer has a shared expert", fn);
+    if (!aligned(x, 16) || (slot_out && !aligned(slot_out, 16)) || !aligned(ws, 256) ||
+        (shared_out && !aligned(shared_out, 16)))
+        return fail(MOE_ERR_INVALID_ARG, "%s: misaligned pointer (x/outputs 16 B, ws 256 B)", fn);
     moe::FfnArgs a = make_args(L, x, x_dt, n_tokens);
     a.topk_idx = topk_idx; a.offsets = expert_offsets; a.perm = perm; a.active = active;
-    a.slot_out = slot_out; a.shared_out = shared_out; a.ws = ws;
+    a.slot_out = slot_out; a.shared_out = shared_out; a.ws = ws; a.stages = stages;
     const int path = choose_path(L, a);
     if (path == MOE_PATH_GEMV && !(moe::ffn_gemv_supported(a)))
-        return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: decode kernels need bf16 x, iq2x/q2k, T <= 4 and "
-                                         "hidden in {512..4096}, supported inter/shared sizes");
+        return fail(MOE_ERR_UNSUPPORTED, "%s: decode kernels need bf16 x, iq2x/q2k, T <= 4 and "
+                                         "hidden in {512..4096}, supported inter/shared sizes", fn);
     if (path == MOE_PATH_GEMM && !(moe::ffn_gemm_supported(a)))
-        return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: grouped-GEMM kernels need bf16 x and hidden, inter, "
-                                         "shared_inter multiples of 256");
+        return fail(MOE_ERR_UNSUPPORTED, "%s: grouped-GEMM kernels need bf16 x and hidden, inter, "
+                                         "shared_inter multiples of 256", fn);
     const size_t need = workspace_for(path, L, n_tokens);
-    if (ws_bytes < need)
-        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: workspace too small (%zu < %zu)", ws_bytes, need);
+    if (ws_bytes < need) return fail(MOE_ERR_INVALID_ARG, "%s: workspace too small (%zu < %zu)", fn, ws_bytes, need);
     hipError_t e;
     if (path == MOE_PATH_GEMV) e = moe::launch_ffn_gemv(a, (hipStream_t)stream);
     else if (path == MOE_PATH_GEMM) e = moe::launch_ffn_gemm(a, (hipStream_t)stream);
     else e = moe::launch_ffn_generic(a, (hipStream_t)stream);
-    return from_hip(e, "moe_expert_ffn");
+    return from_hip(e, fn);
+}
+
+moe_status moe_expert_ffn(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
+                          const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
+                          const int32_t *active, float *slot_out, float *shared_out, void *ws, size_t ws_bytes,
+                          void *stream) {
+    return expert_call("moe_expert_ffn", moe::STAGE_GATE_UP | moe::STAGE_DOWN, L, x, x_dt, n_tokens, topk_idx,
+                       expert_offsets, perm, active, slot_out, shared_out, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_gate_up(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
+                              const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
+                              const int32_t *active, void *ws, size_t ws_bytes, void *stream) {
+    return expert_call("moe_expert_gate_up", moe::STAGE_GATE_UP, L, x, x_dt, n_tokens, topk_idx, expert_offsets,
+                       perm, active, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_down(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
+                           const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
+                           const int32_t *active, float *slot_out, float *shared_out, void *ws, size_t ws_bytes,
+                           void *stream) {
+    return expert_call("moe_expert_down", moe::STAGE_DOWN, L, x, x_dt, n_tokens, topk_idx, expert_offsets, perm,
+                       active, slot_out, shared_out, ws, ws_bytes, stream);
 }
 
 moe_status moe_combine(const float *slot_out, const float *topk_w, const float *shared_out, int32_t n_tokens,

@@ -486,14 +486,16 @@ template <int MAXM>
 hipError_t dispatch(const FfnArgs &a, _Float16 *h, float *hs, hipStream_t st) {
     const int max_active = min(a.T * a.k, a.E);
     hipError_t e = hipErrorInvalidValue;
-    // gate/up: routed rows of H (64 per chunk), shared rows of H (8 per chunk)
-    if (a.H == 4096) e = run_gateup<MAXM, 64, 1, 64, 8>(a, max_active, h, hs, st);
-    else if (a.H == 2048) e = run_gateup<MAXM, 32, 1, 64, 4>(a, max_active, h, hs, st);
-    else if (a.H == 1024) e = run_gateup<MAXM, 16, 1, 64, 2>(a, max_active, h, hs, st);
-    else if (a.H == 512) e = run_gateup<MAXM, 8, 1, 64, 1>(a, max_active, h, hs, st);
-    if (e != hipSuccess) return e;
+    if (a.stages & STAGE_GATE_UP) {
+        // routed rows of H (64 per chunk), shared rows of H (8 per chunk)
+        if (a.H == 4096) e = run_gateup<MAXM, 64, 1, 64, 8>(a, max_active, h, hs, st);
+        else if (a.H == 2048) e = run_gateup<MAXM, 32, 1, 64, 4>(a, max_active, h, hs, st);
+        else if (a.H == 1024) e = run_gateup<MAXM, 16, 1, 64, 2>(a, max_active, h, hs, st);
+        else if (a.H == 512) e = run_gateup<MAXM, 8, 1, 64, 1>(a, max_active, h, hs, st);
+        if (e != hipSuccess) return e;
+    }
+    if (!(a.stages & STAGE_DOWN)) return hipSuccess;
     // down: routed rows of I (64 per chunk), shared rows of Is (8 per chunk)
-    e = hipErrorInvalidValue;
     const int Is = a.Is > 0 ? a.Is : a.I;
 #define MOE_DOWN(I_, LPR_, SI_, SLPR_, SCPL_)                                                       \
     if (a.I == I_ && Is == SI_) return run_down<MAXM, LPR_, 1, SLPR_, SCPL_>(a, max_active, h, hs, st);
@@ -504,7 +506,7 @@ hipError_t dispatch(const FfnArgs &a, _Float16 *h, float *hs, hipStream_t st) {
     MOE_DOWN(2048, 32, 1024, 64, 2)
     MOE_DOWN(1024, 16, 2048, 64, 4)
 #undef MOE_DOWN
-    return e;
+    return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -110,20 +110,27 @@ hipError_t launch_ffn_generic(const FfnArgs &a, hipStream_t st) {
     float *h = static_cast<float *>(a.ws);
     float *hs = h + (size_t)a.T * a.k * a.I;
     const int S = a.T * a.k;
-    if (a.x_bf16) hipLaunchKernelGGL(k_gateup_generic<true>, dim3((a.I + 255) / 256 * S), dim3(256), 0, st, a, h);
-    else hipLaunchKernelGGL(k_gateup_generic<false>, dim3((a.I + 255) / 256 * S), dim3(256), 0, st, a, h);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_down_generic, dim3((a.H + 255) / 256 * S), dim3(256), 0, st, a, h);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (a.Is > 0) {
-        if (a.x_bf16)
-            hipLaunchKernelGGL(k_shared_gateup_generic<true>, dim3((a.Is + 255) / 256 * a.T), dim3(256), 0, st, a, hs);
-        else
-            hipLaunchKernelGGL(k_shared_gateup_generic<false>, dim3((a.Is + 255) / 256 * a.T), dim3(256), 0, st, a, hs);
+    hipError_t e = hipSuccess;
+    if (a.stages & STAGE_GATE_UP) {
+        if (a.x_bf16) hipLaunchKernelGGL(k_gateup_generic<true>, dim3((a.I + 255) / 256 * S), dim3(256), 0, st, a, h);
+        else hipLaunchKernelGGL(k_gateup_generic<false>, dim3((a.I + 255) / 256 * S), dim3(256), 0, st, a, h);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(k_shared_down_generic, dim3((a.H + 255) / 256 * a.T), dim3(256), 0, st, a, hs);
-        e = hipGetLastError();
+        if (a.Is > 0) {
+            if (a.x_bf16)
+                hipLaunchKernelGGL(k_shared_gateup_generic<true>, dim3((a.Is + 255) / 256 * a.T), dim3(256), 0, st, a, hs);
+            else
+                hipLaunchKernelGGL(k_shared_gateup_generic<false>, dim3((a.Is + 255) / 256 * a.T), dim3(256), 0, st, a,
+                                   hs);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    }
+    if (a.stages & STAGE_DOWN) {
+        hipLaunchKernelGGL(k_down_generic, dim3((a.H + 255) / 256 * S), dim3(256), 0, st, a, h);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (a.Is > 0) {
+            hipLaunchKernelGGL(k_shared_down_generic, dim3((a.H + 255) / 256 * a.T), dim3(256), 0, st, a, hs);
+            e = hipGetLastError();
+        }
     }
     return e;
 }

@@ -46,7 +46,9 @@ struct FfnArgs {
     const int32_t *topk_idx, *offsets, *perm, *active;
     float *slot_out, *shared_out;
     void *ws;
+    int stages;                        // bit 0: gate/up + SwiGLU, bit 1: down
 };
+enum { STAGE_GATE_UP = 1, STAGE_DOWN = 2 };
 size_t ffn_workspace_generic(int H, int I, int E, int k, int Is, int T);
 hipError_t launch_ffn_generic(const FfnArgs &a, hipStream_t st);
 size_t ffn_workspace_gemv(int H, int I, int E, int k, int Is, int T);

@@ -179,6 +179,22 @@ moe_status moe_expert_ffn(const moe_layer_desc *L, const void *x, int32_t x_dt, 
                           void *stream);
 
 /*
+ * The two halves of moe_expert_ffn, for callers that schedule them apart (or
+ * time them): moe_expert_gate_up writes the SwiGLU activations h of every slot
+ * and of the shared expert into `ws` (layout private to the library);
+ * moe_expert_down reads them from the same `ws` and writes slot_out and
+ * shared_out.  Same arguments and checks as moe_expert_ffn; both calls must
+ * see the same L, x, n_tokens, routing arrays and ws.
+ */
+moe_status moe_expert_gate_up(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
+                              const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
+                              const int32_t *active, void *ws, size_t ws_bytes, void *stream);
+moe_status moe_expert_down(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
+                           const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
+                           const int32_t *active, float *slot_out, float *shared_out, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/*
  * y[t][c] = sum_{j<k} topk_w[t][j] * slot_out[t*k+j][c] (+ shared_out[t][c]),
  * j in increasing order, fp32.  shared_out may be NULL.
  */
