@@ -205,6 +205,9 @@ def _oracle_layer(L, x):
 LAYER_CASES = [
     ("tiny", 4, 0), ("small", 1, 0), ("small", 3, 0), ("small", 4, 0), ("small", 1, 1), ("small", 37, 1),
     ("mid", 2, 0), ("mid", 9, 1), ("mid_fp32", 3, 0),
+    # grouped-GEMM kernels: auto path above 4 tokens, and forced at the degenerate sizes
+    ("small", 5, 0), ("small", 37, 0), ("small", 1, 3), ("small", 3, 3), ("mid", 70, 0), ("mid", 130, 0),
+    ("mid", 300, 0),
 ]
 
 
@@ -240,6 +243,36 @@ def test_decode_layer_full_size(m, T):
         assert np.array_equal(got["topk_idx"], ref["topk_idx"])
         err = rel_l2_rows(got["y"], ref["y"])
         note(f"  max per-token rel L2 = {err.max():.3e}")
+        assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("name,T,chunk", [("prefill", 512, 512), ("long", 2048, 2048), ("long", 2600, 2048)])
+def test_prefill_layer_full_size_sampled(m, name, T, chunk):
+    """Full-size prefill layers through the grouped-GEMM kernels: every token is
+    computed on the GPU, routing is compared on all tokens, and the outputs of a
+    sample of tokens (the oracle's cost grows with the experts it touches)
+    against the oracle evaluated on those tokens alone (the layer is per-token)."""
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward
+    L = _layer("decode")                       # prefill and long share the decode layer's weights
+    sp = synth.SPECS[name]
+    _, bias = synth.make_router(sp)
+    x = synth.activations(name, T, sp.hidden, True)
+    DL = DeviceLayer.from_synth(L, path=0)
+    DL.bias = None if bias is None else torch.from_numpy(bias).cuda()
+    g = np.random.default_rng(T)
+    for c0 in range(0, T, chunk):
+        xc = x[c0:c0 + chunk]
+        note(f"prefill {name} tokens {c0}..{c0 + xc.shape[0]}")
+        b = LayerBuffers.allocate(DL, xc.shape[0])
+        forward(DL, dev_x(xc), b)
+        torch.cuda.synchronize()
+        _, oi, _ = oracle.route(xc, L.w_router, sp.top_k, bias)
+        assert np.array_equal(b.topk_idx.cpu().numpy(), oi)
+        sample = np.sort(g.choice(xc.shape[0], size=min(6, xc.shape[0]), replace=False))
+        ref = oracle.layer(xc[sample], L.w_router, sp.top_k, sp.n_experts, sp.inter, sp.gate_up_fmt, L.gate, L.up,
+                           sp.down_fmt, L.down, L.codebook, bias=bias, shared=L.shared)
+        err = rel_l2_rows(b.y.cpu().numpy()[sample], ref["y"])
+        note(f"  sampled tokens {sample.tolist()}: max per-token rel L2 = {err.max():.3e}")
         assert err.max() <= TOL
 
 
