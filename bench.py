@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=0, help="launches per kernel timing pass (default: steps)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
+    p.add_argument("--prefill-reps", type=int, default=5)
     return p.parse_args()
 
 
@@ -176,6 +178,12 @@ def main():
                 "bytes_per_launch": nbytes["gate_up"], "avg_launch_us": round(gu_us, 3)}
     step_bw = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
 
+    prefill = None
+    if not args.no_prefill:
+        del g, g2
+        torch.cuda.synchronize()
+        prefill = prefill_bench(L, layers[0], args.prefill_reps)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(L, x_np, args.cpu_seconds)
@@ -192,8 +200,82 @@ def main():
         "cpu_baseline": cpu,
         "step": {"bytes_per_token": nbytes["total"], "effective_GBps": round(step_bw, 1),
                  "hbm_frac": round(step_bw / HBM_PEAK_GBS, 4), "graph_gpu_ms": round(gpu_ms, 3)},
+        "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
+
+
+def prefill_bench(L, DL, reps):
+    """Prefill workloads on the same layer weights: a 512-token chunk with a
+    seeded per-expert router bias (skewed expert load), and the 11,709-token
+    long prompt in 2048-token chunks (5 x 2048 + 1469).  Reported per workload:
+    tokens/s over the whole prompt, and the gate/up grouped-GEMM stage (fp16
+    copy of x + k_gemm_gateup) timed alone with HIP events against the bf16/fp16
+    MFMA peak, counting only the useful FLOPs (selected experts, real tokens)."""
+    import torch
+
+    import synth
+    from bit_quantized_moe_permute_amd import moe_expert_gate_up
+    from bit_quantized_moe_permute_amd.layer import LayerBuffers, forward
+
+    sp = L.spec
+    H, I, k, Is = sp.hidden, sp.inter, sp.top_k, sp.shared_inter
+    out = {}
+    for name, T_total, chunk in (("prefill", 512, 512), ("long", 11709, 2048)):
+        wspec = synth.SPECS[name]
+        _, bias = synth.make_router(wspec)
+        DL.bias = None if bias is None else torch.from_numpy(bias).cuda()
+        x = synth.activations(name, T_total, H, True)
+        xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        chunks = [(c, min(chunk, T_total - c)) for c in range(0, T_total, chunk)]
+        bufs = {n: LayerBuffers.allocate(DL, n) for n in sorted({n for _, n in chunks})}
+
+        def prompt():
+            for c0, n in chunks:
+                forward(DL, xd[c0:c0 + n], bufs[n])
+
+        prompt()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(reps):
+            prompt()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / reps
+        # gate/up stage alone, on the first (largest) chunk
+        c0, n = chunks[0]
+        b = bufs[n]
+        forward(DL, xd[c0:c0 + n], b)
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for _ in range(reps):
+            moe_expert_gate_up(DL.desc, xd[c0:c0 + n], b.topk_idx, b.offsets, b.perm, b.active, b.ws_ffn)
+        f1.record()
+        torch.cuda.synchronize()
+        gu_us = f0.elapsed_time(f1) * 1e3 / reps
+        flops = 4.0 * n * k * H * I + 4.0 * n * H * Is
+        tflops = flops / (gu_us * 1e-6) / 1e12
+        step_flops = 6.0 * T_total * k * H * I + 6.0 * T_total * H * Is
+        counts = np.diff(b.offsets.cpu().numpy())
+        out[name] = {
+            "tokens": T_total, "chunk": chunk, "tokens_per_s": round(T_total / wall, 1),
+            "ms_per_prompt": round(wall * 1e3, 4),
+            "layer_tflops": round(step_flops / wall / 1e12, 2),
+            "gate_up_stage": {"us": round(gu_us, 2), "tokens": n, "flops": flops, "tflops": round(tflops, 2),
+                              "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+                              "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
+            "tokens_per_expert": {"min": int(counts.min()), "max": int(counts.max()),
+                                  "active": int((counts > 0).sum())},
+        }
+        log(f"prefill {name}: {T_total / wall:.0f} tokens/s, gate/up stage {gu_us:.1f} us "
+            f"({tflops:.0f} TFLOP/s)")
+        del bufs
+        torch.cuda.synchronize()
+    DL.bias = None
+    return out
 
 
 def cpu_baseline(L, x_np, budget_s):

@@ -32,9 +32,9 @@ using namespace moe;
 namespace {
 
 constexpr int TOK = 64;          // tokens per tile (2 MFMA A fragments of 32)
-constexpr int ROWS = 256;        // weight rows per workgroup (4 waves x 64)
+constexpr int ROWS = 256;        // weight rows per workgroup (8 waves x 32)
+constexpr int NTHR = 512;        // threads per workgroup
 constexpr int KB = 256;          // K per block (one quant block)
-constexpr int XPITCH = KB + 8;   // LDS row pitch in halves (breaks bank alignment)
 
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
 
@@ -90,11 +90,22 @@ __device__ void tile_scan(const int32_t *offsets, int E, int *tile_off) {
     }
 }
 
-// Workgroup id -> item index: each XCD (ids dealt round-robin over 8) gets a
-// contiguous range of item indices.
-__device__ __forceinline__ int xcd_remap(int p, int G) {
-    const int x = p & 7, slot = p >> 3, q = G >> 3, r = G & 7;
-    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + slot;
+// Workgroup id -> item.  Workgroups are dealt round-robin to the 8 XCDs (id % 8);
+// XCD x runs q_x = G/8 (+1) of them.  Each XCD first takes its even share of the
+// S shared-expert items (the longest ones), then a contiguous run of routed items,
+// so that workgroups sharing an expert's tiles sit on one XCD's L2.
+struct XcdSplit {
+    bool shared;
+    int index;      // into the shared or the routed item list
+};
+__device__ __forceinline__ XcdSplit xcd_remap(int p, int G, int S) {
+    const int x = p & 7, slot = p >> 3;
+    const int gq = G >> 3, gr = G & 7, sq = S >> 3, sr = S & 7;
+    const int s_x = sq + (x < sr ? 1 : 0);
+    if (slot < s_x) return {true, (x < sr ? x * (sq + 1) : sr * (sq + 1) + (x - sr) * sq) + slot};
+    const int pre_q = x < gr ? x * (gq + 1) : gr * (gq + 1) + (x - gr) * gq;
+    const int pre_s = x < sr ? x * (sq + 1) : sr * (sq + 1) + (x - sr) * sq;
+    return {false, pre_q - pre_s + (slot - s_x)};
 }
 
 // rows: weight rows of the routed matrix (I for gate/up, H for down);
@@ -107,18 +118,18 @@ __device__ bool get_item(const FfnArgs &a, int rows, int srows, int *tile_off, I
     const int routed = NT * RT;
     const int RS = a.Is > 0 ? srows / ROWS : 0;
     const int st_tiles = (a.T + TOK - 1) / TOK;
-    const int G = routed + RS * st_tiles;
+    const int S = RS * st_tiles;
+    const int G = routed + S;
     if ((int)blockIdx.x >= G) return false;
-    const int q = xcd_remap(blockIdx.x, G);
-    if (q < routed) {
-        const int tq = q / RT;                 // global token-tile index if row tiles were innermost
-        // find expert: largest e with RT*tile_off[e] <= q
+    const XcdSplit xs = xcd_remap(blockIdx.x, G, S);
+    if (!xs.shared) {
+        const int q = xs.index;
+        // find the expert: largest e with RT*tile_off[e] <= q
         int lo = 0, hi = a.E - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (tile_off[mid] * RT <= q) lo = mid; else hi = mid - 1;
         }
-        (void)tq;
         const int e = lo, nt = tile_off[e + 1] - tile_off[e];
         const int local = q - tile_off[e] * RT;
         const int r = local / nt, t = local % nt;
@@ -127,7 +138,7 @@ __device__ bool get_item(const FfnArgs &a, int rows, int srows, int *tile_off, I
         it.p0 = a.offsets[e] + t * TOK;
         it.n = min(TOK, n_e - t * TOK);
     } else {
-        const int local = q - routed;
+        const int local = xs.index;
         const int r = local / st_tiles, t = local % st_tiles;
         it.shared = 1; it.e = -1; it.r = r;
         it.p0 = t * TOK;
@@ -137,43 +148,86 @@ __device__ bool get_item(const FfnArgs &a, int rows, int srows, int *tile_off, I
 }
 
 // ---------------------------------------------------------------------------
-// A-tile staging: 64 rows x 256 halves of K block kb into LDS (row pitch XPITCH)
-// src_row[m] = pointer to the start of row m (or nullptr: zeros)
+// A tiles in LDS: 64 rows x 256 16-bit values (32 chunks of 16 B per row),
+// chunk c of row m stored at position c ^ (m & 15) so that the 32 lanes of a
+// fragment read (rows 0..31, one chunk) hit distinct banks.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void stage_rows(const uint16_t *const *src_row, int kb, uint16_t *lds) {
-    const int tid = threadIdx.x;
+__device__ __forceinline__ int tpos(int m, int c) { return m * 32 + (c ^ (m & 15)); }
+
+// Tiles are staged through registers: x_fetch issues the global loads of a
+// tile (4 x 16 B per thread, 32 consecutive threads per 512-byte row), the
+// compute of the current tile runs, then x_store writes the registers to LDS.
+struct XStage {
+    uint4 v[4];
+};
+
+// Row pointers are read back from LDS, so the compiler cannot tell they point
+// to global memory; loading through a flat pointer would tie the loads to the
+// LDS wait counter.  Load through an explicit global pointer instead.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_t gbl_u32x4;
+
+__device__ __forceinline__ uint4 gload16(const uint16_t *p) {
+    const u32x4_t v = *(gbl_u32x4 *)(reinterpret_cast<uintptr_t>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// src_row[m]: start of row m (rows past the tile's tokens alias row 0); k0: first column
+__device__ __forceinline__ void x_fetch(const uint16_t *const *src_row, int k0, XStage &xs) {
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int idx = it * 256 + tid;
-        const int m = idx >> 5, c = idx & 31;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        const uint16_t *s = src_row[m];
-        if (s) v = *reinterpret_cast<const uint4 *>(s + (int64_t)kb * KB + 8 * c);
-        *reinterpret_cast<uint4 *>(lds + m * XPITCH + 8 * c) = v;
+    for (int i = 0; i < 4; ++i) {
+        const int idx = threadIdx.x + NTHR * i, m = idx >> 5, c = idx & 31;
+        xs.v[i] = gload16(src_row[m] + k0 + 8 * c);
     }
 }
 
-__device__ __forceinline__ f16x8_t lds_frag16(const uint16_t *lds, int m, int col) {
-    return *reinterpret_cast<const f16x8_t *>(lds + m * XPITCH + col);
-}
-__device__ __forceinline__ bf16x8_t lds_fragbf(const uint16_t *lds, int m, int col) {
-    return *reinterpret_cast<const bf16x8_t *>(lds + m * XPITCH + col);
+// 128-wide K stage of two planes: chunks 0..15 from hi, 16..31 from lo
+__device__ __forceinline__ void x_fetch_hilo(const uint16_t *const *hi, const uint16_t *const *lo, int k0,
+                                             XStage &xs) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = threadIdx.x + NTHR * i, m = idx >> 5, c = idx & 31;
+        const uint16_t *row = c < 16 ? hi[m] : lo[m];
+        xs.v[i] = gload16(row + k0 + 8 * (c & 15));
+    }
 }
 
-// eight fp4 codes (word) -> eight fp16 values times the packed fp16 pair mul
+__device__ __forceinline__ void x_store(const XStage &xs, uint4 *tile) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = threadIdx.x + NTHR * i, m = idx >> 5, c = idx & 31;
+        tile[tpos(m, c)] = xs.v[i];
+    }
+}
+
+
+
+__device__ __forceinline__ f16x8_t frag16(const uint4 *tile, int m, int c) {
+    return __builtin_bit_cast(f16x8_t, tile[tpos(m, c)]);
+}
+__device__ __forceinline__ bf16x8_t fragbf(const uint4 *tile, int m, int c) {
+    return __builtin_bit_cast(bf16x8_t, tile[tpos(m, c)]);
+}
+
+// eight fp4 codes (word) -> eight fp16 values times a packed fp16 pair
 __device__ __forceinline__ f16x8_t fp4x8_f16_mul(uint32_t word, f16x2_t mul) {
-    f16x2_t p0 = fp4x2_f16<0>(word) * mul, p1 = fp4x2_f16<1>(word) * mul;
-    f16x2_t p2 = fp4x2_f16<2>(word) * mul, p3 = fp4x2_f16<3>(word) * mul;
+    const f16x2_t p0 = fp4x2_f16<0>(word) * mul, p1 = fp4x2_f16<1>(word) * mul;
+    const f16x2_t p2 = fp4x2_f16<2>(word) * mul, p3 = fp4x2_f16<3>(word) * mul;
     return f16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
-// q2k codes (value q/2) -> q * sc: scale 2.0 is a power of two, applied exactly by the convert
+// q2k codes (value q/2) -> q * sc: the convert's scale 2.0 is a power of two, applied exactly
 __device__ __forceinline__ f16x8_t q2k_f16_mul(uint32_t codes, f16x2_t sc2) {
-    f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 2.0f, 0) * sc2;
-    f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 2.0f, 1) * sc2;
-    f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 2.0f, 2) * sc2;
-    f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 2.0f, 3) * sc2;
+    const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 2.0f, 0) * sc2;
+    const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 2.0f, 1) * sc2;
+    const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 2.0f, 2) * sc2;
+    const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 2.0f, 3) * sc2;
     return f16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+__device__ __forceinline__ f16x2_t f16pair(uint32_t v) {
+    const _Float16 h = (_Float16)(float)v;
+    return f16x2_t{h, h};
 }
 
 __device__ __forceinline__ void scale_acc(f32x16_t &acc, float s) {
@@ -181,364 +235,478 @@ __device__ __forceinline__ void scale_acc(f32x16_t &acc, float s) {
     for (int i = 0; i < 16; ++i) acc[i] *= s;
 }
 
+// New unit for an accumulator kept in units of the previous block scale:
+// returns the factor to apply and updates prev; a zero scale keeps the unit.
+__device__ __forceinline__ float rescale(float cur, float &prev) {
+    const float dn = cur == 0.f ? prev : cur;
+    const float s = prev * __builtin_amdgcn_rcpf(dn);
+    prev = dn;
+    return s;
+}
+
 // D layout of v_mfma_f32_32x32x16: lane l holds column l % 32 and rows
 // 8*(v/4) + 4*(l/32) + (v%4), v = 0..15.
 __device__ __forceinline__ int drow(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
 // ---------------------------------------------------------------------------
-// gate/up + SwiGLU
+// gate/up + SwiGLU.  Wave w owns weight rows row_base .. row_base+31 of both
+// gate and up (B fragments 0 and 1) for the tile's 64 tokens (A fragments 0, 1).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void k_gemm_gateup(GemmArgs g) {
+struct GuW {
+    uint4 q[2][2];      // [gate/up][chunk]: this lane's 32 bytes of sub-group fields
+    float d[2];         // block scales
+};
+
+__device__ __forceinline__ void gu_load(const FfnArgs &a, int e, int row, int kb, int hh, int64_t nb_row,
+                                        int64_t nb_mat, int64_t NB, GuW &w) {
+    const int64_t bl = (int64_t)e * nb_mat + (int64_t)row * nb_row + kb;
+    const uint8_t *W[2] = {a.gate, a.up};
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const uint8_t *base = W[f] + bl * 64 + hh * 32;
+        w.q[f][0] = *reinterpret_cast<const uint4 *>(base);
+        w.q[f][1] = *reinterpret_cast<const uint4 *>(base + 16);
+        w.d[f] = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(W[f] + NB * 64)[bl]);
+    }
+}
+
+// One 256-wide K block: 16 K-steps x 2 B fragments x (1 or 2) token fragments.
+template <bool two>
+__device__ __forceinline__ void gu_block(const GuW &w, const uint4 *tile, const uint32_t *cb4, const uint32_t *sgn,
+                                         int n, int hh, float (&dprev)[2], f32x16_t (&acc)[2][2]) {
+    f16x2_t mul[2][4];                                   // [gate/up][group]: (2s+1), or 0 for a zero block
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const float sf = rescale(w.d[f], dprev[f]);
+        scale_acc(acc[0][f], sf);
+        if constexpr (two) scale_acc(acc[1][f], sf);
+        const uint32_t keep = w.d[f] == 0.f ? 0u : 0xFFFFFFFFu;
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            const uint4 qq = w.q[f][gi >> 1];
+            const uint32_t lo = (gi & 1) ? qq.z : qq.x, hi = (gi & 1) ? qq.w : qq.y;
+            const uint32_t s = ((lo >> 15) & 1u) | ((lo >> 30) & 2u) | ((hi >> 13) & 4u) | ((hi >> 28) & 8u);
+            mul[f][gi] = f16pair((2u * s + 1u) & keep);
+        }
+    }
+    // phase 1: all 32 codebook/sign lookups of the block at once (one LDS round trip)
+    uint32_t words[2][16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int chunk = j >> 3, fld = j & 7, p = fld & 3;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const uint4 qq = w.q[f][chunk];
+            const uint32_t dw = (fld >> 2) ? ((p < 2) ? qq.z : qq.w) : ((p < 2) ? qq.x : qq.y);
+            const uint32_t fw = (p & 1) ? (dw >> 16) : (dw & 0xFFFFu);
+            words[f][j] = cb4[fw & 0xFFu] | sgn[(fw >> 8) & 0x7Fu];
+        }
+    }
+    // phase 2: convert and multiply on the matrix cores; A fragments read one K-step ahead
+    auto col_chunk = [&](int j) {
+        const int chunk = j >> 3, fld = j & 7;
+        return 4 * (2 * hh + chunk + 4 * (fld >> 2)) + (fld & 3);   // 16-B chunk of column 32*grp + 8p
+    };
+    f16x8_t a0 = frag16(tile, n, col_chunk(0)), a1;
+    if constexpr (two) a1 = frag16(tile, 32 + n, col_chunk(0));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        f16x8_t na0, na1;
+        if (j + 1 < 16) {
+            na0 = frag16(tile, n, col_chunk(j + 1));
+            if constexpr (two) na1 = frag16(tile, 32 + n, col_chunk(j + 1));
+        }
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const f16x8_t b = fp4x8_f16_mul(words[f][j], mul[f][j >> 2]);
+            acc[0][f] = mfma_f16(a0, b, acc[0][f]);
+            if constexpr (two) acc[1][f] = mfma_f16(a1, b, acc[1][f]);
+        }
+        if (j + 1 < 16) {
+            a0 = na0;
+            if constexpr (two) a1 = na1;
+        }
+    }
+}
+
+template <bool two>
+__device__ __forceinline__ void gu_loop(const FfnArgs &a, int e, int row, int hh, int n, const uint16_t *const *src,
+                                        uint4 (*tiles)[TOK * 32], const uint32_t *cb4, const uint32_t *sgn,
+                                        float (&dprev)[2], f32x16_t (&acc)[2][2]) {
+    const int H = a.H, nkb = H / KB;
+    const int64_t nb_row = H / KB, nb_mat = (int64_t)a.I * nb_row, NB = nb_mat * a.E;
+    GuW w0, w1;
+    XStage xs;
+    x_fetch(src, 0, xs);
+    gu_load(a, e, row, 0, hh, nb_row, nb_mat, NB, w0);
+    x_store(xs, tiles[0]);
+    __syncthreads();
+    // every iteration prefetches block min(kb + 1, nkb - 1): no conditional loads
+    for (int kb = 0; kb < nkb; kb += 2) {
+        const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
+        x_fetch(src, k1 * KB, xs);
+        gu_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w1);
+        gu_block<two>(w0, tiles[0], cb4, sgn, n, hh, dprev, acc);
+        x_store(xs, tiles[1]);
+        __syncthreads();
+        if (kb + 1 >= nkb) break;
+        x_fetch(src, k2 * KB, xs);
+        gu_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w0);
+        gu_block<two>(w1, tiles[1], cb4, sgn, n, hh, dprev, acc);
+        x_store(xs, tiles[0]);
+        __syncthreads();
+    }
+}
+
+// Shared expert gate/up: bf16 B fragments straight from the weight rows, read
+// one 64-wide K stage (4 K-steps) ahead into registers; x tiles double-buffered
+// in LDS as for the routed experts.
+typedef bf16x8_t BStage[2][4];       // [gate/up][K-step of the stage]
+
+__device__ __forceinline__ void sg_stage_load(const FfnArgs &a, int row, int hh, int st, BStage &b) {
+    const int kb = st >> 2, j0 = 4 * (st & 3);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int c = 2 * (j0 + jj) + hh;
+        b[0][jj] = *reinterpret_cast<const bf16x8_t *>(a.sg + (int64_t)row * a.H + kb * KB + 8 * c);
+        b[1][jj] = *reinterpret_cast<const bf16x8_t *>(a.su + (int64_t)row * a.H + kb * KB + 8 * c);
+    }
+}
+
+template <bool two>
+__device__ __forceinline__ void sg_stage(const BStage &b, const uint4 *tile, int st, int n, int hh,
+                                         f32x16_t (&acc)[2][2]) {
+    const int j0 = 4 * (st & 3);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int c = 2 * (j0 + jj) + hh;                 // columns 16j + 8hh
+        const bf16x8_t a0 = fragbf(tile, n, c);
+        bf16x8_t a1;
+        if constexpr (two) a1 = fragbf(tile, 32 + n, c);
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            acc[0][f] = mfma_bf16(a0, b[f][jj], acc[0][f]);
+            if constexpr (two) acc[1][f] = mfma_bf16(a1, b[f][jj], acc[1][f]);
+        }
+    }
+}
+
+template <bool two>
+__device__ __forceinline__ void sg_loop(const FfnArgs &a, int row, int hh, int n, const uint16_t *const *src,
+                                        uint4 (*tiles)[TOK * 32], f32x16_t (&acc)[2][2]) {
+    const int nkb = a.H / KB, nst = 4 * nkb;
+    BStage b0, b1;
+    XStage xs;
+    x_fetch(src, 0, xs);
+    sg_stage_load(a, row, hh, 0, b0);
+    x_store(xs, tiles[0]);
+    __syncthreads();
+    for (int st = 0; st < nst; st += 2) {               // two 64-wide stages per iteration, four per block
+        const int kb = st >> 2;
+        const bool block_start = (st & 3) == 0;
+        if (block_start) x_fetch(src, min(kb + 1, nkb - 1) * KB, xs);
+        sg_stage_load(a, row, hh, st + 1, b1);
+        sg_stage<two>(b0, tiles[kb & 1], st, n, hh, acc);
+        sg_stage_load(a, row, hh, min(st + 2, nst - 1), b0);
+        sg_stage<two>(b1, tiles[kb & 1], st + 1, n, hh, acc);
+        if (!block_start) {                              // end of block kb: publish tile kb + 1
+            x_store(xs, tiles[(kb + 1) & 1]);
+            __syncthreads();
+        }
+    }
+}
+
+__global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
     const FfnArgs &a = g.a;
     __shared__ int tile_off[257];
     __shared__ uint32_t cb4[256], sgn[128];
     __shared__ const uint16_t *src[TOK];
     __shared__ int dst[TOK];
-    __shared__ __attribute__((aligned(16))) uint16_t xs[TOK * XPITCH];
+    __shared__ uint4 tiles[2][TOK * 32];
     Item it;
     if (!get_item(a, a.I, a.Is, tile_off, it)) return;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
     const int H = a.H;
     if (!it.shared) {
-        for (int i = tid; i < 256; i += 256) cb4[i] = codebook_row_fp4(a.codebook, i);
-        for (int i = tid; i < 128; i += 256) sgn[i] = sign_spread(i);
+        if (tid < 256) cb4[tid] = codebook_row_fp4(a.codebook, tid);
+        else if (tid < 384) sgn[tid - 256] = sign_spread(tid - 256);
     }
     if (tid < TOK) {
-        const uint16_t *s = nullptr;
-        int d = -1;
-        if (tid < it.n) {
-            if (!it.shared) {
-                const int p = it.p0 + tid;
-                s = reinterpret_cast<const uint16_t *>(g.x16) + (int64_t)(a.perm[p] / a.k) * H;
-                d = p;
-            } else {
-                s = static_cast<const uint16_t *>(a.x) + (int64_t)(it.p0 + tid) * H;
-                d = it.p0 + tid;
-            }
-        }
+        const int m = tid < it.n ? tid : 0;                  // rows past the tile alias row 0
+        const uint16_t *s;
+        if (!it.shared) s = reinterpret_cast<const uint16_t *>(g.x16) + (int64_t)(a.perm[it.p0 + m] / a.k) * H;
+        else s = static_cast<const uint16_t *>(a.x) + (int64_t)(it.p0 + m) * H;
         src[tid] = s;
-        dst[tid] = d;
+        dst[tid] = tid < it.n ? it.p0 + tid : -1;
     }
     __syncthreads();
-
-    f32x16_t acc[2][4];          // [token frag][gate rt0, gate rt1, up rt0, up rt1]
+    const bool two = it.n > 32;
+    f32x16_t acc[2][2];          // [token frag][gate, up]
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
-
-    const int row_base = it.r * ROWS + wv * 64;          // this wave's 64 rows
-    const int nkb = H / KB;
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+    const int row = it.r * ROWS + wv * 32 + n;           // this lane's weight row
 
     if (!it.shared) {
-        const int64_t nb_row = H / KB, nb_mat = (int64_t)a.I * nb_row, NB = nb_mat * a.E;
-        const uint8_t *W[2] = {a.gate, a.up};
-        float dprev[4] = {1.f, 1.f, 1.f, 1.f};
-        for (int kb = 0; kb < nkb; ++kb) {
-            // this lane's 32 bytes of fields for its 4 rows (chunks 2hh, 2hh+1) and the block scales
-            uint4 q[4][2];
-            float dcur[4];
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const int row = row_base + (f & 1) * 32 + n;
-                const int64_t bl = (int64_t)it.e * nb_mat + (int64_t)row * nb_row + kb;
-                const uint8_t *base = W[f >> 1] + bl * 64 + hh * 32;
-                q[f][0] = *reinterpret_cast<const uint4 *>(base);
-                q[f][1] = *reinterpret_cast<const uint4 *>(base + 16);
-                dcur[f] = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(W[f >> 1] + NB * 64)[bl]);
-            }
-            __syncthreads();                                   // previous block's readers are done
-            stage_rows(src, kb, xs);
-            // rescale accumulators into units of this block's d (d == 0: the block adds nothing)
-            bool zero[4];
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                zero[f] = dcur[f] == 0.f;
-                const float dn = zero[f] ? dprev[f] : dcur[f];
-                const float s = dprev[f] / dn;
-                scale_acc(acc[0][f], s);
-                scale_acc(acc[1][f], s);
-                dprev[f] = dn;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int chunk = j >> 3, fld = j & 7;                        // within this lane's 32 B
-                const int grp = 2 * hh + chunk + 4 * (fld >> 2), p = fld & 3;
-                const int col = 32 * grp + 8 * p;
-                const f16x8_t a0 = lds_frag16(xs, n, col);
-                const f16x8_t a1 = lds_frag16(xs, 32 + n, col);
-#pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    const uint4 qq = q[f][chunk];
-                    const uint32_t lo = (fld >> 2) ? qq.z : qq.x, hi = (fld >> 2) ? qq.w : qq.y;
-                    const uint32_t s = ((lo >> 15) & 1u) | ((lo >> 30) & 2u) | ((hi >> 13) & 4u) | ((hi >> 28) & 8u);
-                    const _Float16 m1 = zero[f] ? (_Float16)0.0f : (_Float16)(float)(2 * s + 1);
-                    const uint32_t fw = ((p < 2 ? lo : hi) >> (16 * (p & 1))) & 0xFFFFu;
-                    const uint32_t word = cb4[fw & 0xFFu] | sgn[(fw >> 8) & 0x7Fu];
-                    const f16x8_t b = fp4x8_f16_mul(word, f16x2_t{m1, m1});
-                    acc[0][f] = mfma_f16(a0, b, acc[0][f]);
-                    acc[1][f] = mfma_f16(a1, b, acc[1][f]);
-                }
-            }
-        }
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            scale_acc(acc[0][f], dprev[f]);
-            scale_acc(acc[1][f], dprev[f]);
-        }
+        float dprev[2] = {1.f, 1.f};
+        if (two) gu_loop<true>(a, it.e, row, hh, n, src, tiles, cb4, sgn, dprev, acc);
+        else gu_loop<false>(a, it.e, row, hh, n, src, tiles, cb4, sgn, dprev, acc);
         // SwiGLU epilogue: h[position][row] in fp16
 #pragma unroll
         for (int tf = 0; tf < 2; ++tf)
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = 32 * tf + drow(v, lane);
-                    const int d = dst[m];
-                    if (d >= 0)
-                        g.h[(int64_t)d * a.I + row_base + 32 * rt + n] =
-                            (_Float16)silu_mul(acc[tf][rt][v], acc[tf][2 + rt][v]);
-                }
-    } else {
-        const uint16_t *W[2] = {a.sg, a.su};
-        for (int kb = 0; kb < nkb; ++kb) {
-            __syncthreads();
-            stage_rows(src, kb, xs);
-            __syncthreads();
-#pragma unroll 4
-            for (int j = 0; j < 16; ++j) {
-                const int col = 16 * j + 8 * hh;
-                const bf16x8_t a0 = lds_fragbf(xs, n, col);
-                const bf16x8_t a1 = lds_fragbf(xs, 32 + n, col);
-#pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    const int row = row_base + (f & 1) * 32 + n;
-                    const bf16x8_t b = *reinterpret_cast<const bf16x8_t *>(W[f >> 1] + (int64_t)row * H + kb * KB + col);
-                    acc[0][f] = mfma_bf16(a0, b, acc[0][f]);
-                    acc[1][f] = mfma_bf16(a1, b, acc[1][f]);
-                }
+            for (int v = 0; v < 16; ++v) {
+                const int d = dst[32 * tf + drow(v, lane)];
+                if (d >= 0)
+                    g.h[(int64_t)d * a.I + row] =
+                        (_Float16)silu_mul(acc[tf][0][v] * dprev[0], acc[tf][1][v] * dprev[1]);
             }
-        }
+    } else {
+        if (two) sg_loop<true>(a, row, hh, n, src, tiles, acc);
+        else sg_loop<false>(a, row, hh, n, src, tiles, acc);
 #pragma unroll
         for (int tf = 0; tf < 2; ++tf)
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = 32 * tf + drow(v, lane);
-                    const int d = dst[m];
-                    if (d >= 0) {
-                        const float hv = silu_mul(acc[tf][rt][v], acc[tf][2 + rt][v]);
-                        const uint32_t hb = __float_as_uint(hv);
-                        const uint32_t hi = (hb + 0x7FFFu + ((hb >> 16) & 1u)) >> 16;   // bf16, nearest even
-                        const float rest = hv - __uint_as_float(hi << 16);
-                        const uint32_t rb = __float_as_uint(rest);
-                        const uint32_t lo = (rb + 0x7FFFu + ((rb >> 16) & 1u)) >> 16;
-                        const int64_t o = (int64_t)d * a.Is + row_base + 32 * rt + n;
-                        g.hs_hi[o] = (uint16_t)hi;
-                        g.hs_lo[o] = (uint16_t)lo;
-                    }
+            for (int v = 0; v < 16; ++v) {
+                const int d = dst[32 * tf + drow(v, lane)];
+                if (d >= 0) {
+                    const float hv = silu_mul(acc[tf][0][v], acc[tf][1][v]);
+                    const uint32_t hb = __float_as_uint(hv);
+                    const uint32_t hi = (hb + 0x7FFFu + ((hb >> 16) & 1u)) >> 16;   // bf16, nearest even
+                    const float rest = hv - __uint_as_float(hi << 16);
+                    const uint32_t rb = __float_as_uint(rest);
+                    const uint32_t lo = (rb + 0x7FFFu + ((rb >> 16) & 1u)) >> 16;
+                    const int64_t o = (int64_t)d * a.Is + row;
+                    g.hs_hi[o] = (uint16_t)hi;
+                    g.hs_lo[o] = (uint16_t)lo;
                 }
+            }
     }
 }
 
 // ---------------------------------------------------------------------------
-// down projection
+// down projection.  Wave w owns output rows row_base .. row_base+31.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void k_gemm_down(GemmArgs g) {
+struct DnW {
+    uint4 q[2];         // [chunk]: 32 bytes = sub-blocks 8hh .. 8hh+7
+    uint2 sm;           // their (sc | m << 4) bytes
+    float d, dm;
+};
+
+__device__ __forceinline__ void dn_load(const FfnArgs &a, int e, int row, int kb, int hh, int64_t nb_row,
+                                        int64_t nb_mat, int64_t NB, DnW &w) {
+    const uint8_t *Q = a.down, *S = a.down + NB * 64;
+    const uint32_t *D = reinterpret_cast<const uint32_t *>(a.down + NB * 80);
+    const int64_t bl = (int64_t)e * nb_mat + (int64_t)row * nb_row + kb;
+    w.q[0] = *reinterpret_cast<const uint4 *>(Q + bl * 64 + hh * 32);
+    w.q[1] = *reinterpret_cast<const uint4 *>(Q + bl * 64 + hh * 32 + 16);
+    w.sm = *reinterpret_cast<const uint2 *>(S + bl * 16 + hh * 8);
+    const uint32_t dd = D[bl];
+    w.d = f16_bits_to_f32(dd & 0xFFFFu);
+    w.dm = f16_bits_to_f32(dd >> 16);
+}
+
+// per-16 sums of the h tile (fp16 hi + lo), 512 threads = 64 rows x 8 pairs of sub-blocks
+__device__ __forceinline__ void tile_sums(const uint4 *tile, _Float16 (*hs)[TOK][16]) {
+    const int m = threadIdx.x >> 3, qd = threadIdx.x & 7;
+#pragma unroll
+    for (int sbq = 0; sbq < 2; ++sbq) {
+        const int sb = 2 * qd + sbq;
+        float s = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            const uint4 u = tile[tpos(m, 2 * sb + cc)];
+            const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f16x2_t pr = __builtin_bit_cast(f16x2_t, wds[i]);
+                s += (float)pr.x + (float)pr.y;
+            }
+        }
+        const _Float16 shi = (_Float16)s;
+        hs[0][m][sb] = shi;
+        hs[1][m][sb] = (_Float16)(s - (float)shi);
+    }
+}
+
+template <bool two>
+__device__ __forceinline__ void dn_block(const DnW &w, const uint4 *tile, _Float16 (*hs)[TOK][16], int n, int hh,
+                                         float &dprev, float &mprev, f32x16_t (&acc)[2], f32x16_t (&accm)[2]) {
+    const float s1 = rescale(w.d, dprev), s2 = rescale(w.dm, mprev);
+    scale_acc(acc[0], s1);
+    scale_acc(accm[0], s2);
+    if constexpr (two) {
+        scale_acc(acc[1], s1);
+        scale_acc(accm[1], s2);
+    }
+    const uint32_t kq = w.d == 0.f ? 0u : 0xFFu, km = w.dm == 0.f ? 0u : 0xFFu;
+    f16x2_t scp[8];
+    f16x8_t mins;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t byte = (i < 4 ? w.sm.x >> (8 * i) : w.sm.y >> (8 * (i - 4))) & 0xFFu;
+        scp[i] = f16pair(byte & 15u & kq);
+        mins[i] = (_Float16)(float)((byte >> 4) & km);
+    }
+    // main term: K-step j covers sub-block 8hh + j/2, half j%2 (columns 16*(8hh+j/2) + 8*(j%2))
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int sbl = j >> 1, half = j & 1;
+        const int c = 2 * (8 * hh + sbl) + half;
+        const f16x8_t a0 = frag16(tile, n, c);
+        const uint4 qq = w.q[sbl >> 2];
+        const uint32_t dw = (sbl & 3) == 0 ? qq.x : ((sbl & 3) == 1 ? qq.y : ((sbl & 3) == 2 ? qq.z : qq.w));
+        const uint32_t codes = half ? ((dw >> 2) & 0x33333333u) : (dw & 0x33333333u);
+        const f16x8_t b = q2k_f16_mul(codes, scp[sbl]);
+        acc[0] = mfma_f16(a0, b, acc[0]);
+        if constexpr (two) acc[1] = mfma_f16(frag16(tile, 32 + n, c), b, acc[1]);
+    }
+    // min term: K = the 16 sub-blocks; A = per-16 sums (hi, lo), B = mins
+    accm[0] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[0][n][8 * hh]), mins, accm[0]);
+    accm[0] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[1][n][8 * hh]), mins, accm[0]);
+    if constexpr (two) {
+        accm[1] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[0][32 + n][8 * hh]), mins, accm[1]);
+        accm[1] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[1][32 + n][8 * hh]), mins, accm[1]);
+    }
+}
+
+template <bool two>
+__device__ __forceinline__ void dn_loop(const FfnArgs &a, int e, int row, int hh, int n, const uint16_t *const *src,
+                                        uint4 (*tiles)[TOK * 32], _Float16 (*hsum)[TOK][16], float &dprev,
+                                        float &mprev, f32x16_t (&acc)[2], f32x16_t (&accm)[2]) {
+    const int I = a.I, H = a.H, nkb = I / KB;
+    const int64_t nb_row = I / KB, nb_mat = (int64_t)H * nb_row, NB = nb_mat * a.E;
+    DnW w0, w1;
+    XStage xs;
+    x_fetch(src, 0, xs);
+    dn_load(a, e, row, 0, hh, nb_row, nb_mat, NB, w0);
+    x_store(xs, tiles[0]);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; kb += 2) {
+        const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
+        tile_sums(tiles[0], hsum);
+        __syncthreads();
+        x_fetch(src, k1 * KB, xs);
+        dn_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w1);
+        dn_block<two>(w0, tiles[0], hsum, n, hh, dprev, mprev, acc, accm);
+        x_store(xs, tiles[1]);
+        __syncthreads();
+        if (kb + 1 >= nkb) break;
+        tile_sums(tiles[1], hsum);
+        __syncthreads();
+        x_fetch(src, k2 * KB, xs);
+        dn_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w0);
+        dn_block<two>(w1, tiles[1], hsum, n, hh, dprev, mprev, acc, accm);
+        x_store(xs, tiles[0]);
+        __syncthreads();
+    }
+}
+
+// Shared expert down: A = h as bf16 hi + lo.  One LDS tile holds a 128-wide K
+// stage of both planes (chunks 0..15 = hi, 16..31 = lo), double-buffered; the
+// bf16 B fragments of the stage (8 K-steps) are read into registers one stage
+// ahead.
+typedef bf16x8_t DStage[8];
+
+__device__ __forceinline__ void sd_stage_load(const FfnArgs &a, int row, int hh, int st, DStage &b) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+        b[jj] = *reinterpret_cast<const bf16x8_t *>(a.sd + (int64_t)row * a.Is + st * 128 + 16 * jj + 8 * hh);
+}
+
+template <bool two>
+__device__ __forceinline__ void sd_stage(const DStage &b, const uint4 *tile, int n, int hh, f32x16_t (&acc)[2]) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+        const int c = 2 * jj + hh;
+        acc[0] = mfma_bf16(fragbf(tile, n, c), b[jj], acc[0]);
+        acc[0] = mfma_bf16(fragbf(tile, n, 16 + c), b[jj], acc[0]);
+        if constexpr (two) {
+            acc[1] = mfma_bf16(fragbf(tile, 32 + n, c), b[jj], acc[1]);
+            acc[1] = mfma_bf16(fragbf(tile, 32 + n, 16 + c), b[jj], acc[1]);
+        }
+    }
+}
+
+template <bool two>
+__device__ __forceinline__ void sd_loop(const FfnArgs &a, int row, int hh, int n, const uint16_t *const *hi,
+                                        const uint16_t *const *lo, uint4 (*tiles)[TOK * 32], f32x16_t (&acc)[2]) {
+    const int nst = a.Is / 128;
+    DStage b0, b1;
+    XStage xs;
+    x_fetch_hilo(hi, lo, 0, xs);
+    sd_stage_load(a, row, hh, 0, b0);
+    x_store(xs, tiles[0]);
+    __syncthreads();
+    for (int st = 0; st < nst; st += 2) {
+        const int s1 = min(st + 1, nst - 1), s2 = min(st + 2, nst - 1);
+        x_fetch_hilo(hi, lo, s1 * 128, xs);
+        sd_stage_load(a, row, hh, s1, b1);
+        sd_stage<two>(b0, tiles[0], n, hh, acc);
+        x_store(xs, tiles[1]);
+        __syncthreads();
+        if (st + 1 >= nst) break;
+        x_fetch_hilo(hi, lo, s2 * 128, xs);
+        sd_stage_load(a, row, hh, s2, b0);
+        sd_stage<two>(b1, tiles[1], n, hh, acc);
+        x_store(xs, tiles[0]);
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
     const FfnArgs &a = g.a;
     __shared__ int tile_off[257];
     __shared__ const uint16_t *src[TOK];
     __shared__ const uint16_t *src_lo[TOK];
     __shared__ int dst[TOK];
-    __shared__ __attribute__((aligned(16))) uint16_t xs[TOK * XPITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t xs2[TOK * XPITCH];      // shared: lo plane
-    __shared__ __attribute__((aligned(16))) uint16_t hsum[2][TOK * 24];      // routed: per-16 sums, hi/lo
+    __shared__ uint4 tiles[2][TOK * 32];
+    __shared__ __attribute__((aligned(16))) _Float16 hsum[2][TOK][16];
     Item it;
     if (!get_item(a, a.H, a.H, tile_off, it)) return;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
     const int I = a.I, H = a.H;
     if (tid < TOK) {
-        const uint16_t *s = nullptr, *s2 = nullptr;
-        int d = -1;
-        if (tid < it.n) {
-            if (!it.shared) {
-                const int p = it.p0 + tid;
-                s = reinterpret_cast<const uint16_t *>(g.h) + (int64_t)p * I;
-                d = a.perm[p];                                   // output slot
-            } else {
-                s = g.hs_hi + (int64_t)(it.p0 + tid) * a.Is;
-                s2 = g.hs_lo + (int64_t)(it.p0 + tid) * a.Is;
-                d = it.p0 + tid;
-            }
+        const int m = tid < it.n ? tid : 0;
+        if (!it.shared) {
+            src[tid] = reinterpret_cast<const uint16_t *>(g.h) + (int64_t)(it.p0 + m) * I;
+            src_lo[tid] = nullptr;
+            dst[tid] = tid < it.n ? a.perm[it.p0 + tid] : -1;          // output slot
+        } else {
+            src[tid] = g.hs_hi + (int64_t)(it.p0 + m) * a.Is;
+            src_lo[tid] = g.hs_lo + (int64_t)(it.p0 + m) * a.Is;
+            dst[tid] = tid < it.n ? it.p0 + tid : -1;
         }
-        src[tid] = s;
-        src_lo[tid] = s2;
-        dst[tid] = d;
     }
     __syncthreads();
-
-    const int row_base = it.r * ROWS + wv * 64;
+    const bool two = it.n > 32;
+    const int row = it.r * ROWS + wv * 32 + n;           // this lane's output row
+    f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
     if (!it.shared) {
-        f32x16_t acc[2][2], accm[2][2];      // [token frag][row tile]
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) { acc[i][j] = f32x16_t{}; accm[i][j] = f32x16_t{}; }
-        const int64_t nb_row = I / KB, nb_mat = (int64_t)H * nb_row, NB = nb_mat * a.E;
-        const uint8_t *Q = a.down, *S = a.down + NB * 64;
-        const uint32_t *D = reinterpret_cast<const uint32_t *>(a.down + NB * 80);
-        float dprev[2] = {1.f, 1.f}, mprev[2] = {1.f, 1.f};
-        const int nkb = I / KB;
-        for (int kb = 0; kb < nkb; ++kb) {
-            uint4 q[2][2];
-            uint2 sm[2];
-            float dcur[2], mcur[2];
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const int row = row_base + 32 * rt + n;
-                const int64_t bl = (int64_t)it.e * nb_mat + (int64_t)row * nb_row + kb;
-                q[rt][0] = *reinterpret_cast<const uint4 *>(Q + bl * 64 + hh * 32);
-                q[rt][1] = *reinterpret_cast<const uint4 *>(Q + bl * 64 + hh * 32 + 16);
-                sm[rt] = *reinterpret_cast<const uint2 *>(S + bl * 16 + hh * 8);
-                const uint32_t dd = D[bl];
-                dcur[rt] = f16_bits_to_f32(dd & 0xFFFFu);
-                mcur[rt] = f16_bits_to_f32(dd >> 16);
-            }
-            __syncthreads();
-            stage_rows(src, kb, xs);
-            // per-16 sums of the staged h rows: 256 threads = 64 rows x 4 quarters of 64 columns
-            {
-                const int m = tid >> 2, qd = tid & 3;
-                const uint16_t *row = src[m];
-#pragma unroll
-                for (int sbq = 0; sbq < 4; ++sbq) {
-                    float s = 0.f;
-                    if (row) {
-                        const uint4 u0 = *reinterpret_cast<const uint4 *>(row + (int64_t)kb * KB + 64 * qd + 16 * sbq);
-                        const uint4 u1 = *reinterpret_cast<const uint4 *>(row + (int64_t)kb * KB + 64 * qd + 16 * sbq + 8);
-                        const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            const f16x2_t pr = __builtin_bit_cast(f16x2_t, w[i]);
-                            s += (float)pr.x + (float)pr.y;
-                        }
-                    }
-                    const _Float16 shi = (_Float16)s;
-                    const _Float16 slo = (_Float16)(s - (float)shi);
-                    hsum[0][m * 24 + 4 * qd + sbq] = __builtin_bit_cast(uint16_t, shi);
-                    hsum[1][m * 24 + 4 * qd + sbq] = __builtin_bit_cast(uint16_t, slo);
-                }
-            }
-            bool zq[2], zm[2];
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                zq[rt] = dcur[rt] == 0.f;
-                zm[rt] = mcur[rt] == 0.f;
-                const float dn = zq[rt] ? dprev[rt] : dcur[rt];
-                const float mn = zm[rt] ? mprev[rt] : mcur[rt];
-                const float s1 = dprev[rt] / dn, s2 = mprev[rt] / mn;
-                scale_acc(acc[0][rt], s1);
-                scale_acc(acc[1][rt], s1);
-                scale_acc(accm[0][rt], s2);
-                scale_acc(accm[1][rt], s2);
-                dprev[rt] = dn;
-                mprev[rt] = mn;
-            }
-            __syncthreads();
-            // main term: K-step j covers sub-block 8*hh + j/2, half j%2
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int sbl = j >> 1, half = j & 1;
-                const int col = 16 * (8 * hh + sbl) + 8 * half;
-                const f16x8_t a0 = lds_frag16(xs, n, col);
-                const f16x8_t a1 = lds_frag16(xs, 32 + n, col);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const uint4 qq = q[rt][sbl >> 2];
-                    const uint32_t dw = (sbl & 3) == 0 ? qq.x : ((sbl & 3) == 1 ? qq.y : ((sbl & 3) == 2 ? qq.z : qq.w));
-                    const uint32_t codes = half ? ((dw >> 2) & 0x33333333u) : (dw & 0x33333333u);
-                    const uint32_t scb = (sbl < 4 ? sm[rt].x >> (8 * sbl) : sm[rt].y >> (8 * (sbl - 4))) & 15u;
-                    const _Float16 sc = zq[rt] ? (_Float16)0.0f : (_Float16)(float)scb;
-                    const f16x8_t b = q2k_f16_mul(codes, f16x2_t{sc, sc});
-                    acc[0][rt] = mfma_f16(a0, b, acc[0][rt]);
-                    acc[1][rt] = mfma_f16(a1, b, acc[1][rt]);
-                }
-            }
-            // min term: K = the 16 sub-blocks; A = per-16 sums (hi, lo), B = mins
-            {
-                const f16x8_t ah0 = *reinterpret_cast<const f16x8_t *>(&hsum[0][n * 24 + 8 * hh]);
-                const f16x8_t ah1 = *reinterpret_cast<const f16x8_t *>(&hsum[0][(32 + n) * 24 + 8 * hh]);
-                const f16x8_t al0 = *reinterpret_cast<const f16x8_t *>(&hsum[1][n * 24 + 8 * hh]);
-                const f16x8_t al1 = *reinterpret_cast<const f16x8_t *>(&hsum[1][(32 + n) * 24 + 8 * hh]);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    f16x8_t b;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const uint32_t byte = (i < 4 ? sm[rt].x >> (8 * i) : sm[rt].y >> (8 * (i - 4))) & 0xFFu;
-                        b[i] = zm[rt] ? (_Float16)0.0f : (_Float16)(float)(byte >> 4);
-                    }
-                    accm[0][rt] = mfma_f16(ah0, b, accm[0][rt]);
-                    accm[0][rt] = mfma_f16(al0, b, accm[0][rt]);
-                    accm[1][rt] = mfma_f16(ah1, b, accm[1][rt]);
-                    accm[1][rt] = mfma_f16(al1, b, accm[1][rt]);
-                }
-            }
-        }
+        f32x16_t accm[2] = {f32x16_t{}, f32x16_t{}};
+        float dprev = 1.f, mprev = 1.f;
+        if (two) dn_loop<true>(a, it.e, row, hh, n, src, tiles, hsum, dprev, mprev, acc, accm);
+        else dn_loop<false>(a, it.e, row, hh, n, src, tiles, hsum, dprev, mprev, acc, accm);
 #pragma unroll
         for (int tf = 0; tf < 2; ++tf)
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = 32 * tf + drow(v, lane);
-                    const int d = dst[m];
-                    if (d >= 0)
-                        a.slot_out[(int64_t)d * H + row_base + 32 * rt + n] =
-                            acc[tf][rt][v] * dprev[rt] - accm[tf][rt][v] * mprev[rt];
-                }
+            for (int v = 0; v < 16; ++v) {
+                const int d = dst[32 * tf + drow(v, lane)];
+                if (d >= 0) a.slot_out[(int64_t)d * H + row] = acc[tf][v] * dprev - accm[tf][v] * mprev;
+            }
     } else {
-        f32x16_t acc[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
-        const int Is = a.Is, nkb = Is / KB;
-        for (int kb = 0; kb < nkb; ++kb) {
-            __syncthreads();
-            stage_rows(src, kb, xs);
-            stage_rows(src_lo, kb, xs2);
-            __syncthreads();
-#pragma unroll 4
-            for (int j = 0; j < 16; ++j) {
-                const int col = 16 * j + 8 * hh;
-                const bf16x8_t h0 = lds_fragbf(xs, n, col), h1 = lds_fragbf(xs, 32 + n, col);
-                const bf16x8_t l0 = lds_fragbf(xs2, n, col), l1 = lds_fragbf(xs2, 32 + n, col);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const int row = row_base + 32 * rt + n;
-                    const bf16x8_t b = *reinterpret_cast<const bf16x8_t *>(a.sd + (int64_t)row * Is + kb * KB + col);
-                    acc[0][rt] = mfma_bf16(h0, b, acc[0][rt]);
-                    acc[0][rt] = mfma_bf16(l0, b, acc[0][rt]);
-                    acc[1][rt] = mfma_bf16(h1, b, acc[1][rt]);
-                    acc[1][rt] = mfma_bf16(l1, b, acc[1][rt]);
-                }
-            }
-        }
+        if (two) sd_loop<true>(a, row, hh, n, src, src_lo, tiles, acc);
+        else sd_loop<false>(a, row, hh, n, src, src_lo, tiles, acc);
 #pragma unroll
         for (int tf = 0; tf < 2; ++tf)
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = 32 * tf + drow(v, lane);
-                    const int d = dst[m];
-                    if (d >= 0) a.shared_out[(int64_t)d * H + row_base + 32 * rt + n] = acc[tf][rt][v];
-                }
+            for (int v = 0; v < 16; ++v) {
+                const int d = dst[32 * tf + drow(v, lane)];
+                if (d >= 0) a.shared_out[(int64_t)d * H + row] = acc[tf][v];
+            }
     }
 }
 
@@ -608,12 +776,12 @@ hipError_t launch_ffn_gemm(const FfnArgs &a, hipStream_t st) {
                            static_cast<const uint16_t *>(a.x), const_cast<_Float16 *>(g.x16), n8);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int G = max_tiles * (a.I / ROWS) + (a.Is > 0 ? st_tiles * (a.Is / ROWS) : 0);
-        hipLaunchKernelGGL(k_gemm_gateup, dim3(G), dim3(256), 0, st, g);
+        hipLaunchKernelGGL(k_gemm_gateup, dim3(G), dim3(NTHR), 0, st, g);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (a.stages & STAGE_DOWN) {
         const int G = max_tiles * (a.H / ROWS) + (a.Is > 0 ? st_tiles * (a.H / ROWS) : 0);
-        hipLaunchKernelGGL(k_gemm_down, dim3(G), dim3(256), 0, st, g);
+        hipLaunchKernelGGL(k_gemm_down, dim3(G), dim3(NTHR), 0, st, g);
         e = hipGetLastError();
     }
     return e;
