@@ -21,7 +21,7 @@ Workloads (layer shapes; all inputs seeded):
 Full-size routed experts (1.8 GB of blocks per layer) are drawn field by field
 ("random blocks"): every bit pattern of the formats decodes to a valid block,
 so scales are drawn from distributions measured once on N(0,0.02) weights
-quantized by the reference encoders (block scale, group/sub-block scales and
+quantized by the oracle's quantizers (block scale, group/sub-block scales and
 mins), codes and signs are uniform random bits, and the iq2x block scale is
 set so that the decoded weights have mean ~0 and RMS ~0.02-0.026 like
 N(0,0.02) weights.
