@@ -16,7 +16,9 @@
 //        sub-block j, nibble i carries q[16j+i] in bits 0..1 and q[16j+8+i] in
 //        bits 2..3, so (v & 0x33333333) and ((v >> 2) & 0x33333333) are eight
 //        fp4 codes each.  S keeps the canonical (sc | m << 4) bytes.
-//  q4k   Q: NB x 128 B (canonical nibble order: 16 B per 32-weight sub-block),
+//  q4k   Q: NB x 128 B, one u32 per 8 consecutive weights w0..w7 with the
+//        code of w(2i+h) at bits 16h + 4i (so (word >> 4i) & 0x000F000F holds
+//        the pair w(2i), w(2i+1) in its two 16-bit halves),
 //        M: NB x 16 B = d | dmin | u32 low nibbles of fields 0..7 | u32 low
 //        nibbles of fields 8..15 | u32 top two bits of field f at bits 2f.
 //
@@ -94,6 +96,11 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Code of weight i (0..7) in a prepared q4k word.
+__device__ __forceinline__ uint32_t q4k_code(uint32_t word, int i) {
+    return (word >> (16 * (i & 1) + 4 * (i >> 1))) & 15u;
+}
+
 // q4k field f (6 bits) from the prepared 16-byte meta record.
 __device__ __forceinline__ uint32_t q4k_field(uint32_t lo8, uint32_t hi8, uint32_t top, int f) {
     uint32_t nib = f < 8 ? (lo8 >> (4 * f)) & 15u : (hi8 >> (4 * (f - 8))) & 15u;
@@ -152,7 +159,7 @@ __device__ __forceinline__ void q4k_sub8(const uint8_t *prep, int64_t NB, int64_
     float sc = f16_bits_to_f32(M[0] & 0xFFFF) * (float)q4k_field(M[1], M[2], M[3], j);
     float mn = f16_bits_to_f32(M[0] >> 16) * (float)q4k_field(M[1], M[2], M[3], 8 + j);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = sc * (float)((v >> (4 * i)) & 15u) - mn;
+    for (int i = 0; i < 8; ++i) w[i] = sc * (float)q4k_code(v, i) - mn;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }

@@ -108,12 +108,13 @@ __device__ __forceinline__ XcdSplit xcd_remap(int p, int G, int S) {
     return {false, pre_q - pre_s + (slot - s_x)};
 }
 
-// rows: weight rows of the routed matrix (I for gate/up, H for down);
-// srows: rows of the shared matrix (Is for gate/up, H for down).
-__device__ bool get_item(const FfnArgs &a, int rows, int srows, int *tile_off, Item &it) {
+// rows: weight rows of the routed matrix (I for gate/up, H for down), cut
+// into items of rpi rows; srows: rows of the shared matrix (Is for gate/up, H
+// for down), cut into items of ROWS rows.
+__device__ bool get_item(const FfnArgs &a, int rows, int rpi, int srows, int *tile_off, Item &it) {
     tile_scan(a.offsets, a.E, tile_off);
     __syncthreads();
-    const int RT = rows / ROWS;
+    const int RT = rows / rpi;
     const int NT = tile_off[a.E];
     const int routed = NT * RT;
     const int RS = a.Is > 0 ? srows / ROWS : 0;
@@ -164,7 +165,6 @@ struct XStage {
 // Row pointers are read back from LDS, so the compiler cannot tell they point
 // to global memory; loading through a flat pointer would tie the loads to the
 // LDS wait counter.  Load through an explicit global pointer instead.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4_t gbl_u32x4;
 
 __device__ __forceinline__ uint4 gload16(const uint16_t *p) {
@@ -358,6 +358,130 @@ __device__ __forceinline__ void gu_loop(const FfnArgs &a, int e, int row, int hh
     }
 }
 
+// ---------------------------------------------------------------------------
+// q4k routed rows (gate, up or down).  A wave owns 32 rows of ONE matrix; lane
+// (n, hh) holds half hh of row n's block: sub-blocks 4hh .. 4hh+3, 64 bytes of
+// codes, one u32 per K-step.  Codes become exact fp16 integers sc*q through
+// (1024 + q) * sc - 1024 * sc in one fused multiply-add (1024 + q is the fp16
+// pattern 0x6400 | q).  The mins use per-32 sums of the activation tile, kept
+// as fp16 hi + lo and fed to one MFMA per block: lane hh supplies
+// {hi of sub-blocks 4hh..4hh+3, lo of the same} against {m, m}.
+// ---------------------------------------------------------------------------
+struct Q4W {
+    uint4 q[4];
+    uint4 meta;         // d | dmin, low nibbles of sc0..7, low nibbles of m0..7, top bits
+};
+
+__device__ __forceinline__ void q4_load(const uint8_t *W, int64_t NB, int64_t bl, int hh, Q4W &w) {
+    const uint4 *Q = reinterpret_cast<const uint4 *>(W + bl * 128 + hh * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w.q[i] = Q[i];
+    w.meta = *reinterpret_cast<const uint4 *>(W + NB * 128 + bl * 16);
+}
+
+__device__ __forceinline__ f16x8_t q4_f16(uint32_t word, f16x2_t sc2, f16x2_t nsc2) {
+    f16x8_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = ((word >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+        const f16x2_t p = __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, t), sc2, nsc2);
+        r[2 * i] = p.x;
+        r[2 * i + 1] = p.y;
+    }
+    return r;
+}
+
+// Store a fetched tile to LDS and its per-32 sums to hs (hs[m] = {hi 0..3,
+// lo 0..3, hi 4..7, lo 4..7}).  The four chunks of a sub-block sit in four
+// consecutive lanes; they reduce with two cross-lane steps.
+__device__ __forceinline__ void x_store_sums32(const XStage &xs, uint4 *tile, _Float16 (*hs)[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = threadIdx.x + NTHR * i, m = idx >> 5, c = idx & 31;
+        tile[tpos(m, c)] = xs.v[i];
+        const uint32_t wds[4] = {xs.v[i].x, xs.v[i].y, xs.v[i].z, xs.v[i].w};
+        float sm = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const f16x2_t pr = __builtin_bit_cast(f16x2_t, wds[k]);
+            sm += (float)pr.x + (float)pr.y;
+        }
+        sm += __shfl_xor(sm, 1, 64);
+        sm += __shfl_xor(sm, 2, 64);
+        if ((c & 3) == 0) {
+            const int sb = c >> 2;
+            const _Float16 hi = (_Float16)sm;
+            hs[m][8 * (sb >> 2) + (sb & 3)] = hi;
+            hs[m][8 * (sb >> 2) + 4 + (sb & 3)] = (_Float16)(sm - (float)hi);
+        }
+    }
+}
+
+template <bool two>
+__device__ __forceinline__ void q4_block(const Q4W &w, const uint4 *tile, const _Float16 (*hs)[16], int n, int hh,
+                                         float &dprev, float &mprev, f32x16_t (&acc)[2], f32x16_t (&accm)[2]) {
+    const float d = f16_bits_to_f32(w.meta.x & 0xFFFFu), dm = f16_bits_to_f32(w.meta.x >> 16);
+    const float s1 = rescale(d, dprev), s2 = rescale(dm, mprev);
+    scale_acc(acc[0], s1);
+    scale_acc(accm[0], s2);
+    if constexpr (two) {
+        scale_acc(acc[1], s1);
+        scale_acc(accm[1], s2);
+    }
+    const uint32_t kq = d == 0.f ? 0u : 0xFFu, km = dm == 0.f ? 0u : 0xFFu;
+    f16x2_t scp[4], nsc[4];
+    f16x8_t mins;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int sb = 4 * hh + jj;
+        const uint32_t sc = q4k_field(w.meta.y, w.meta.z, w.meta.w, sb) & kq;
+        const uint32_t m = q4k_field(w.meta.y, w.meta.z, w.meta.w, 8 + sb) & km;
+        scp[jj] = f16pair(sc);
+        const _Float16 ns = (_Float16)(-1024.f * (float)sc);
+        nsc[jj] = f16x2_t{ns, ns};
+        mins[jj] = mins[4 + jj] = (_Float16)(float)m;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int c = 16 * hh + j;
+        const uint4 qq = w.q[j >> 2];
+        const uint32_t word = (j & 3) == 0 ? qq.x : ((j & 3) == 1 ? qq.y : ((j & 3) == 2 ? qq.z : qq.w));
+        const f16x8_t b = q4_f16(word, scp[j >> 2], nsc[j >> 2]);
+        acc[0] = mfma_f16(frag16(tile, n, c), b, acc[0]);
+        if constexpr (two) acc[1] = mfma_f16(frag16(tile, 32 + n, c), b, acc[1]);
+    }
+    accm[0] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[n][8 * hh]), mins, accm[0]);
+    if constexpr (two) accm[1] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[32 + n][8 * hh]), mins, accm[1]);
+}
+
+// W: prepared q4k stack (NB blocks); bl0: first block of this lane's row; nkb: blocks per row.
+template <bool two>
+__device__ __forceinline__ void q4_loop(const uint8_t *W, int64_t NB, int64_t bl0, int nkb, int n, int hh,
+                                        const uint16_t *const *src, uint4 (*tiles)[TOK * 32],
+                                        _Float16 (*hs)[TOK][16], float &dprev, float &mprev, f32x16_t (&acc)[2],
+                                        f32x16_t (&accm)[2]) {
+    Q4W w0, w1;
+    XStage xs;
+    x_fetch(src, 0, xs);
+    q4_load(W, NB, bl0, hh, w0);
+    x_store_sums32(xs, tiles[0], hs[0]);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; kb += 2) {
+        const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
+        x_fetch(src, k1 * KB, xs);
+        q4_load(W, NB, bl0 + k1, hh, w1);
+        q4_block<two>(w0, tiles[0], hs[0], n, hh, dprev, mprev, acc, accm);
+        x_store_sums32(xs, tiles[1], hs[1]);
+        __syncthreads();
+        if (kb + 1 >= nkb) break;
+        x_fetch(src, k2 * KB, xs);
+        q4_load(W, NB, bl0 + k2, hh, w0);
+        q4_block<two>(w1, tiles[1], hs[1], n, hh, dprev, mprev, acc, accm);
+        x_store_sums32(xs, tiles[0], hs[0]);
+        __syncthreads();
+    }
+}
+
 // Shared expert gate/up: bf16 B fragments straight from the weight rows, read
 // one 64-wide K stage (4 K-steps) ahead into registers; x tiles double-buffered
 // in LDS as for the routed experts.
@@ -416,19 +540,26 @@ __device__ __forceinline__ void sg_loop(const FfnArgs &a, int row, int hh, int n
     }
 }
 
+// FG: routed gate/up format.  iq2x: a wave owns 32 rows of gate AND up (256
+// rows per item, SwiGLU in registers).  q4k: waves 0-3 own 32 gate rows each,
+// waves 4-7 the same 128 rows of up (128 rows per item); the up values meet
+// the gate values in LDS for the SwiGLU.
+template <int FG>
 __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
     const FfnArgs &a = g.a;
+    constexpr int RPI = FG == FMT_Q4K ? ROWS / 2 : ROWS;
     __shared__ int tile_off[257];
     __shared__ uint32_t cb4[256], sgn[128];
     __shared__ const uint16_t *src[TOK];
     __shared__ int dst[TOK];
     __shared__ uint4 tiles[2][TOK * 32];
+    __shared__ __attribute__((aligned(16))) _Float16 hsum[2][TOK][16];
     Item it;
-    if (!get_item(a, a.I, a.Is, tile_off, it)) return;
+    if (!get_item(a, a.I, RPI, a.Is, tile_off, it)) return;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
     const int H = a.H;
-    if (!it.shared) {
+    if (FG == FMT_IQ2X && !it.shared) {
         if (tid < 256) cb4[tid] = codebook_row_fp4(a.codebook, tid);
         else if (tid < 384) sgn[tid - 256] = sign_spread(tid - 256);
     }
@@ -447,9 +578,38 @@ __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
-    const int row = it.r * ROWS + wv * 32 + n;           // this lane's weight row
+    const int row = it.r * ROWS + wv * 32 + n;           // this lane's weight row (iq2x, shared)
 
-    if (!it.shared) {
+    if (FG == FMT_Q4K && !it.shared) {
+        const bool up = wv >= 4;
+        const int r4 = it.r * RPI + (wv & 3) * 32 + n;
+        const int nkb = H / KB;
+        const int64_t NB = (int64_t)a.E * a.I * nkb, bl0 = ((int64_t)it.e * a.I + r4) * nkb;
+        f32x16_t accq[2] = {f32x16_t{}, f32x16_t{}}, accm[2] = {f32x16_t{}, f32x16_t{}};
+        float dprev = 1.f, mprev = 1.f;
+        if (two) q4_loop<true>(up ? a.up : a.gate, NB, bl0, nkb, n, hh, src, tiles, hsum, dprev, mprev, accq, accm);
+        else q4_loop<false>(up ? a.up : a.gate, NB, bl0, nkb, n, hh, src, tiles, hsum, dprev, mprev, accq, accm);
+        float *xch = reinterpret_cast<float *>(&tiles[0][0]);     // [4 waves][TOK][32] up values
+        if (up) {
+#pragma unroll
+            for (int tf = 0; tf < 2; ++tf)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    xch[((wv & 3) * TOK + 32 * tf + drow(v, lane)) * 32 + n] = accq[tf][v] * dprev - accm[tf][v] * mprev;
+        }
+        __syncthreads();
+        if (!up) {
+#pragma unroll
+            for (int tf = 0; tf < 2; ++tf)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int tt = 32 * tf + drow(v, lane), d = dst[tt];
+                    if (d >= 0)
+                        g.h[(int64_t)d * a.I + r4] = (_Float16)silu_mul(accq[tf][v] * dprev - accm[tf][v] * mprev,
+                                                                        xch[((wv & 3) * TOK + tt) * 32 + n]);
+                }
+        }
+    } else if (!it.shared) {
         float dprev[2] = {1.f, 1.f};
         if (two) gu_loop<true>(a, it.e, row, hh, n, src, tiles, cb4, sgn, dprev, acc);
         else gu_loop<false>(a, it.e, row, hh, n, src, tiles, cb4, sgn, dprev, acc);
@@ -656,6 +816,8 @@ __device__ __forceinline__ void sd_loop(const FfnArgs &a, int row, int hh, int n
     }
 }
 
+// FD: routed down format (q2k or q4k).
+template <int FD>
 __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
     const FfnArgs &a = g.a;
     __shared__ int tile_off[257];
@@ -665,7 +827,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
     __shared__ uint4 tiles[2][TOK * 32];
     __shared__ __attribute__((aligned(16))) _Float16 hsum[2][TOK][16];
     Item it;
-    if (!get_item(a, a.H, a.H, tile_off, it)) return;
+    if (!get_item(a, a.H, ROWS, a.H, tile_off, it)) return;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
     const int I = a.I, H = a.H;
@@ -688,8 +850,15 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
     if (!it.shared) {
         f32x16_t accm[2] = {f32x16_t{}, f32x16_t{}};
         float dprev = 1.f, mprev = 1.f;
-        if (two) dn_loop<true>(a, it.e, row, hh, n, src, tiles, hsum, dprev, mprev, acc, accm);
-        else dn_loop<false>(a, it.e, row, hh, n, src, tiles, hsum, dprev, mprev, acc, accm);
+        if constexpr (FD == FMT_Q4K) {
+            const int nkb = I / KB;
+            const int64_t NB = (int64_t)a.E * H * nkb, bl0 = ((int64_t)it.e * H + row) * nkb;
+            if (two) q4_loop<true>(a.down, NB, bl0, nkb, n, hh, src, tiles, hsum, dprev, mprev, acc, accm);
+            else q4_loop<false>(a.down, NB, bl0, nkb, n, hh, src, tiles, hsum, dprev, mprev, acc, accm);
+        } else {
+            if (two) dn_loop<true>(a, it.e, row, hh, n, src, tiles, hsum, dprev, mprev, acc, accm);
+            else dn_loop<false>(a, it.e, row, hh, n, src, tiles, hsum, dprev, mprev, acc, accm);
+        }
 #pragma unroll
         for (int tf = 0; tf < 2; ++tf)
 #pragma unroll
@@ -746,7 +915,9 @@ Layout layout(int H, int I, int k, int Is, int T) {
 namespace moe {
 
 bool ffn_gemm_supported(const FfnArgs &a) {
-    if (!a.x_bf16 || a.fmt_gu != FMT_IQ2X || a.fmt_d != FMT_Q2K) return false;
+    if (!a.x_bf16) return false;
+    if (a.fmt_gu != FMT_IQ2X && a.fmt_gu != FMT_Q4K) return false;
+    if (a.fmt_d != FMT_Q2K && a.fmt_d != FMT_Q4K) return false;
     if (a.H % 256 || a.I % 256 || (a.Is > 0 && a.Is % 256)) return false;
     if (a.E > 256) return false;
     return true;
@@ -775,13 +946,16 @@ hipError_t launch_ffn_gemm(const FfnArgs &a, hipStream_t st) {
         hipLaunchKernelGGL(k_x_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
                            static_cast<const uint16_t *>(a.x), const_cast<_Float16 *>(g.x16), n8);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int G = max_tiles * (a.I / ROWS) + (a.Is > 0 ? st_tiles * (a.Is / ROWS) : 0);
-        hipLaunchKernelGGL(k_gemm_gateup, dim3(G), dim3(NTHR), 0, st, g);
+        const int rpi = a.fmt_gu == FMT_Q4K ? ROWS / 2 : ROWS;
+        const int G = max_tiles * (a.I / rpi) + (a.Is > 0 ? st_tiles * (a.Is / ROWS) : 0);
+        if (a.fmt_gu == FMT_Q4K) hipLaunchKernelGGL(k_gemm_gateup<FMT_Q4K>, dim3(G), dim3(NTHR), 0, st, g);
+        else hipLaunchKernelGGL(k_gemm_gateup<FMT_IQ2X>, dim3(G), dim3(NTHR), 0, st, g);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (a.stages & STAGE_DOWN) {
         const int G = max_tiles * (a.H / ROWS) + (a.Is > 0 ? st_tiles * (a.H / ROWS) : 0);
-        hipLaunchKernelGGL(k_gemm_down, dim3(G), dim3(NTHR), 0, st, g);
+        if (a.fmt_d == FMT_Q4K) hipLaunchKernelGGL(k_gemm_down<FMT_Q4K>, dim3(G), dim3(NTHR), 0, st, g);
+        else hipLaunchKernelGGL(k_gemm_down<FMT_Q2K>, dim3(G), dim3(NTHR), 0, st, g);
         e = hipGetLastError();
     }
     return e;

@@ -56,7 +56,15 @@ __global__ void k_prep_q4k(const uint8_t *__restrict__ canon, uint8_t *__restric
     const uint8_t *c = canon + b * 144;
     uint8_t *Q = prep + b * 128;
     uint32_t *M = reinterpret_cast<uint32_t *>(prep + NB * 128 + b * 16);
-    for (int i = 0; i < 128; ++i) Q[i] = c[16 + i];
+    for (int u = 0; u < 32; ++u) {                     // 8 weights per word, pairs in the two halves
+        uint32_t v = 0;
+        for (int i = 0; i < 8; ++i) {
+            const int n = 8 * u + i;
+            const uint32_t q = (c[16 + n / 2] >> (4 * (n % 2))) & 15u;
+            v |= q << (16 * (i & 1) + 4 * (i >> 1));
+        }
+        reinterpret_cast<uint32_t *>(Q)[u] = v;
+    }
     uint32_t lo8 = 0, hi8 = 0, top = 0;
     for (int f = 0; f < 16; ++f) {
         uint32_t v = 0;
@@ -138,7 +146,7 @@ __global__ void k_dequant_q4k(const uint8_t *__restrict__ prep, int64_t NB, int6
     float sc = d * (float)q4k_field(M[1], M[2], M[3], j);
     float mn = dmin * (float)q4k_field(M[1], M[2], M[3], 8 + j);
     float *o = out + t * 8;
-    for (int i = 0; i < 8; ++i) o[i] = sc * (float)((v >> (4 * i)) & 15u) - mn;
+    for (int i = 0; i < 8; ++i) o[i] = sc * (float)q4k_code(v, i) - mn;
 }
 
 }  // namespace

@@ -164,13 +164,15 @@ SPECS = {
     # reduced layers that the oracle finishes in seconds; several tiles and a ragged tail
     "small": LayerSpec("small", 512, 256, 16, 4, 256, True, 101),
     "small_q4k": LayerSpec("small_q4k", 512, 256, 16, 4, 256, True, 101, FMT_Q4K, FMT_Q4K),
+    "small_mix_a": LayerSpec("small_mix_a", 512, 256, 16, 4, 256, True, 101, FMT_IQ2X, FMT_Q4K),
+    "small_mix_b": LayerSpec("small_mix_b", 512, 256, 16, 4, 256, True, 101, FMT_Q4K, FMT_Q2K),
     "mid": LayerSpec("mid", 1024, 512, 32, 8, 512, True, 102, bias_std=0.5),
     "mid_fp32": LayerSpec("mid_fp32", 1024, 512, 32, 8, 0, False, 103),
 }
 
 # activation seeds per workload
 X_SEEDS = {"tiny": 0, "decode": 11, "verify": 12, "prefill": 13, "long": 14, "long_q4k": 14,
-           "small": 201, "small_q4k": 201, "mid": 202, "mid_fp32": 203}
+           "small": 201, "small_q4k": 201, "small_mix_a": 201, "small_mix_b": 201, "mid": 202, "mid_fp32": 203}
 BIAS_SEEDS = {"prefill": 23, "mid": 24}
 TOKENS = {"tiny": 4, "decode": 1000, "verify": 3 * 334, "prefill": 512, "long": 11709, "long_q4k": 11709}
 

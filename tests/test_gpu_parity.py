@@ -208,6 +208,9 @@ LAYER_CASES = [
     # grouped-GEMM kernels: auto path above 4 tokens, and forced at the degenerate sizes
     ("small", 5, 0), ("small", 37, 0), ("small", 1, 3), ("small", 3, 3), ("mid", 70, 0), ("mid", 130, 0),
     ("mid", 300, 0),
+    # q4k routed experts (4.5 bpw) and mixed formats: decode sizes and grouped GEMM
+    ("small_q4k", 1, 0), ("small_q4k", 3, 0), ("small_q4k", 37, 0), ("small_q4k", 3, 3), ("small_q4k", 70, 0),
+    ("small_mix_a", 2, 0), ("small_mix_a", 37, 0), ("small_mix_b", 2, 0), ("small_mix_b", 37, 0),
 ]
 
 
@@ -246,14 +249,16 @@ def test_decode_layer_full_size(m, T):
         assert err.max() <= TOL
 
 
-@pytest.mark.parametrize("name,T,chunk", [("prefill", 512, 512), ("long", 2048, 2048), ("long", 2600, 2048)])
+@pytest.mark.parametrize("name,T,chunk", [("prefill", 512, 512), ("long", 2048, 2048), ("long", 2600, 2048),
+                                          ("long_q4k", 2048, 2048)])
 def test_prefill_layer_full_size_sampled(m, name, T, chunk):
     """Full-size prefill layers through the grouped-GEMM kernels: every token is
     computed on the GPU, routing is compared on all tokens, and the outputs of a
     sample of tokens (the oracle's cost grows with the experts it touches)
     against the oracle evaluated on those tokens alone (the layer is per-token)."""
     from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward
-    L = _layer("decode")                       # prefill and long share the decode layer's weights
+    # prefill and long share the decode layer's weights; long_q4k has its own 4-bit experts
+    L = _layer("long_q4k" if name == "long_q4k" else "decode")
     sp = synth.SPECS[name]
     _, bias = synth.make_router(sp)
     x = synth.activations(name, T, sp.hidden, True)
