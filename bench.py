@@ -47,7 +47,46 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
     p.add_argument("--prefill-reps", type=int, default=5)
+    p.add_argument("--no-q4k", action="store_true", help="skip the 4-bit (q4k) routed-expert workloads")
+    p.add_argument("--verify-steps", type=int, default=334, help="steps of the 3-token verify micro-batch")
     return p.parse_args()
+
+
+def graph_steps(step, K, W):
+    """Warm up W steps eagerly, capture K steps in one HIP graph, check one
+    replay against an eager recomputation of the last step, then time one
+    replay.  Returns (wall seconds, event milliseconds)."""
+    import torch
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(K):
+                y_last = step(i)
+    torch.cuda.synchronize()
+    g.replay()                                   # one untimed replay
+    torch.cuda.synchronize()
+    y_graph = y_last.clone()
+    step(K - 1)                                  # eager recomputation of the last step
+    torch.cuda.synchronize()
+    if not torch.equal(y_graph, y_last):
+        raise RuntimeError("graph replay and eager run disagree")
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu_ms = ev0.elapsed_time(ev1)
+    del g
+    torch.cuda.synchronize()
+    return wall, gpu_ms
 
 
 def decode_bytes(H, I, E, k, Is):
@@ -97,44 +136,31 @@ def main():
     bufs = [LayerBuffers.allocate(layers[0], 1) for _ in range(2)]
 
     def step(i):
-        forward(layers[i % args.layers], x[i % n_tok: i % n_tok + 1], bufs[i % 2])
+        b = bufs[i % 2]
+        forward(layers[i % args.layers], x[i % n_tok: i % n_tok + 1], b)
+        return b.y
 
-    log(f"warmup {W} steps (eager)")
-    for i in range(W):
-        step(i)
-    torch.cuda.synchronize()
-
-    # capture exactly K steps in one graph
-    log(f"capturing {K} steps in a HIP graph")
-    g = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(g, stream=cap):
-            for i in range(K):
-                step(i)
-    torch.cuda.synchronize()
-    g.replay()                                   # one untimed replay
-    torch.cuda.synchronize()
-    y_graph = bufs[(K - 1) % 2].y.clone()
-    step(K - 1)                                  # eager recomputation of the last step
-    torch.cuda.synchronize()
-    if not torch.equal(y_graph, bufs[(K - 1) % 2].y):
-        raise RuntimeError("graph replay and eager run disagree")
-
-    log("timed region")
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start = time.perf_counter()
-    ev0.record()
-    g.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    gpu_ms = ev0.elapsed_time(ev1)
+    log(f"decode: warmup {W} steps, {K} steps captured in a HIP graph")
+    wall, gpu_ms = graph_steps(step, K, W)
     ms_per_step = wall * 1e3 / K
     value = K / wall
     log(f"{K} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms -> {value:.0f} tokens/s")
+
+    # speculative-verify micro-batch: 3 independent tokens per step
+    vx_np = synth.activations("verify", 3 * args.verify_steps, H, True)
+    vx = torch.from_numpy(vx_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    vbufs = [LayerBuffers.allocate(layers[0], 3) for _ in range(2)]
+
+    def vstep(i):
+        b = vbufs[i % 2]
+        forward(layers[i % args.layers], vx[3 * i: 3 * i + 3], b)
+        return b.y
+
+    vK = args.verify_steps
+    vwall, _ = graph_steps(vstep, vK, min(W, vK))
+    verify = {"tokens_per_step": 3, "steps": vK, "tokens_per_s": round(3 * vK / vwall, 1),
+              "us_per_step": round(vwall * 1e6 / vK, 2)}
+    log(f"verify: {vK} steps of 3 tokens -> {3 * vK / vwall:.0f} tokens/s, {vwall * 1e6 / vK:.1f} us/step")
 
     # dominant kernel: gate/up (+SwiGLU) GEMV, routed and shared rows in one launch
     reps = args.kernel_reps or K
@@ -153,6 +179,8 @@ def main():
                   b0.ws_route, bias=Li.bias)
     torch.cuda.synchronize()
     g2 = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cap):
         with torch.cuda.graph(g2, stream=cap):
             for i in range(reps):
@@ -178,11 +206,38 @@ def main():
                 "bytes_per_launch": nbytes["gate_up"], "avg_launch_us": round(gu_us, 3)}
     step_bw = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
 
+    del g2
+    torch.cuda.synchronize()
     prefill = None
     if not args.no_prefill:
-        del g, g2
+        prefill = prefill_bench(L, layers[0], args.prefill_reps, ("prefill", "long"))
+
+    decode_q4k = None
+    if not args.no_q4k:
+        # 4-bit routed experts: decode B=1 over cycled copies, and the long prompt
+        del layers[1:]
         torch.cuda.synchronize()
-        prefill = prefill_bench(L, layers[0], args.prefill_reps)
+        log("generating the q4k layer (seeded random blocks)")
+        L4 = synth.make_layer(synth.SPECS["long_q4k"])
+        n4 = max(2, args.layers // 2)
+        layers4 = [DeviceLayer.from_synth(L4, device=dev)]
+        for _ in range(n4 - 1):
+            layers4.append(layers4[0].clone())
+        torch.cuda.synchronize()
+
+        def qstep(i):
+            b = bufs[i % 2]
+            forward(layers4[i % n4], x[i % n_tok: i % n_tok + 1], b)
+            return b.y
+
+        qwall, _ = graph_steps(qstep, K, W)
+        decode_q4k = {"tokens_per_s": round(K / qwall, 1), "ms_per_step": round(qwall * 1e3 / K, 5),
+                      "layer_copies": n4}
+        log(f"decode q4k: {K / qwall:.0f} tokens/s")
+        if not args.no_prefill:
+            prefill.update(prefill_bench(L4, layers4[0], args.prefill_reps, ("long_q4k",)))
+        del layers4
+        torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -200,15 +255,18 @@ def main():
         "cpu_baseline": cpu,
         "step": {"bytes_per_token": nbytes["total"], "effective_GBps": round(step_bw, 1),
                  "hbm_frac": round(step_bw / HBM_PEAK_GBS, 4), "graph_gpu_ms": round(gpu_ms, 3)},
+        "verify": verify,
+        "decode_q4k": decode_q4k,
         "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
 
 
-def prefill_bench(L, DL, reps):
-    """Prefill workloads on the same layer weights: a 512-token chunk with a
-    seeded per-expert router bias (skewed expert load), and the 11,709-token
-    long prompt in 2048-token chunks (5 x 2048 + 1469).  Reported per workload:
+def prefill_bench(L, DL, reps, names):
+    """Prefill workloads on layer DL: a 512-token chunk with a seeded per-expert
+    router bias (skewed expert load, "prefill"), and the 11,709-token long
+    prompt in 2048-token chunks (5 x 2048 + 1469; "long" with 2-bit experts,
+    "long_q4k" with q4k experts).  Reported per workload:
     tokens/s over the whole prompt, and the gate/up grouped-GEMM stage (fp16
     copy of x + k_gemm_gateup) timed alone with HIP events against the bf16/fp16
     MFMA peak, counting only the useful FLOPs (selected experts, real tokens)."""
@@ -221,7 +279,9 @@ def prefill_bench(L, DL, reps):
     sp = L.spec
     H, I, k, Is = sp.hidden, sp.inter, sp.top_k, sp.shared_inter
     out = {}
-    for name, T_total, chunk in (("prefill", 512, 512), ("long", 11709, 2048)):
+    shapes = {"prefill": (512, 512), "long": (11709, 2048), "long_q4k": (11709, 2048)}
+    for name in names:
+        T_total, chunk = shapes[name]
         wspec = synth.SPECS[name]
         _, bias = synth.make_router(wspec)
         DL.bias = None if bias is None else torch.from_numpy(bias).cuda()

@@ -226,7 +226,7 @@ static moe_status expert_call(const char *fn, int stages, const moe_layer_desc *
     a.slot_out = slot_out; a.shared_out = shared_out; a.ws = ws; a.stages = stages;
     const int path = choose_path(L, a);
     if (path == MOE_PATH_GEMV && !(moe::ffn_gemv_supported(a)))
-        return fail(MOE_ERR_UNSUPPORTED, "%s: decode kernels need bf16 x, iq2x/q2k, T <= 4 and "
+        return fail(MOE_ERR_UNSUPPORTED, "%s: decode kernels need bf16 x, T <= 4 and "
                                          "hidden in {512..4096}, supported inter/shared sizes", fn);
     if (path == MOE_PATH_GEMM && !(moe::ffn_gemm_supported(a)))
         return fail(MOE_ERR_UNSUPPORTED, "%s: grouped-GEMM kernels need bf16 x and hidden, inter, "

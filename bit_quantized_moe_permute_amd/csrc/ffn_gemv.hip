@@ -152,6 +152,99 @@ __device__ void routed_gateup(const FfnArgs &a, int e, const Tokens<MAXM> &tk, i
     }
 }
 
+// q4k chunk: 16 B = the 32 codes of sub-block j of a block (meta: the block's
+// d | dmin and packed 6-bit fields).  Codes enter the dot products as bf16
+// 128 + q (pattern 0x4300 | q; pairs sit in the two halves of a prepared word),
+// so per sub-block  sum w x = d sc P - (128 d sc + dmin m) X  with P the dot
+// of the offset codes and X the sum of the 32 activations.
+template <int MAXM>
+__device__ __forceinline__ void q4k_chunk_bf16(uint4 q, uint4 meta, int j, const uint32_t (&xr)[MAXM][16],
+                                               const float (&xs)[MAXM], float (&acc)[MAXM]) {
+    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+    float P[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) P[m] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bf16x2_t t = __builtin_bit_cast(bf16x2_t, ((qw[w] >> (4 * i)) & 0x000F000Fu) | 0x43004300u);
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) P[m] = dot2_bf16(t, __builtin_bit_cast(bf16x2_t, xr[m][4 * w + i]), P[m]);
+        }
+    const float sc = f16_bits_to_f32(meta.x & 0xFFFFu) * (float)q4k_field(meta.y, meta.z, meta.w, j);
+    const float off = __fmaf_rn(f16_bits_to_f32(meta.x >> 16), (float)q4k_field(meta.y, meta.z, meta.w, 8 + j),
+                                128.f * sc);
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) acc[m] += __fmaf_rn(sc, P[m], -off * xs[m]);
+}
+
+// Routed q4k gate/up: a lane covers chunks cp + LPR*i (32 weights each) of a row of H = 32*LPR*CPL.
+template <int LPR, int CPL, int MAXM, int NR>
+__device__ void routed_gateup_q4k(const FfnArgs &a, int e, const Tokens<MAXM> &tk, int row0,
+                                  _Float16 *__restrict__ h) {
+    constexpr int RPI = 64 / LPR;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int cp = lane % LPR, rsub = lane / LPR;
+    const int H = a.H, I = a.I;
+    const int64_t nb_row = H / MOE_QK, nb_mat = (int64_t)I * nb_row, NB = nb_mat * a.E;
+    uint32_t xr[CPL][MAXM][16];
+    float xs[CPL][MAXM];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int ch = cp + LPR * i;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const int t = tk.tok[m < tk.n ? m : 0];
+            const uint4 *xa = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + (int64_t)t * H + 32 * ch);
+            float sum = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint4 u = xa[v];
+                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    xr[i][m][4 * v + k] = w4[k];
+                    sum += __uint_as_float(w4[k] << 16) + __uint_as_float(w4[k] & 0xFFFF0000u);
+                }
+            }
+            xs[i][m] = sum;
+        }
+    }
+    uint4 gq[NR][CPL], uq[NR][CPL], gm[NR][CPL], um[NR][CPL];
+#pragma unroll
+    for (int jr = 0; jr < NR; ++jr) {
+        const int r = min(row0 + (wv * NR + jr) * RPI + rsub, I - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int ch = cp + LPR * i;
+            const int64_t bl = (int64_t)e * nb_mat + (int64_t)r * nb_row + (ch >> 3);
+            gq[jr][i] = *reinterpret_cast<const uint4 *>(a.gate + bl * 128 + (ch & 7) * 16);
+            uq[jr][i] = *reinterpret_cast<const uint4 *>(a.up + bl * 128 + (ch & 7) * 16);
+            gm[jr][i] = *reinterpret_cast<const uint4 *>(a.gate + NB * 128 + bl * 16);
+            um[jr][i] = *reinterpret_cast<const uint4 *>(a.up + NB * 128 + bl * 16);
+        }
+    }
+#pragma unroll
+    for (int jr = 0; jr < NR; ++jr) {
+        float ga[MAXM], ua[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) { ga[m] = 0.f; ua[m] = 0.f; }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int j = (cp + LPR * i) & 7;
+            q4k_chunk_bf16<MAXM>(gq[jr][i], gm[jr][i], j, xr[i], xs[i], ga);
+            q4k_chunk_bf16<MAXM>(uq[jr][i], um[jr][i], j, xr[i], xs[i], ua);
+        }
+        const int r = row0 + (wv * NR + jr) * RPI + rsub;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const float g = row_sum<LPR>(ga[m]), u = row_sum<LPR>(ua[m]);
+            if (m < tk.n && cp == 0 && r < I) h[(int64_t)tk.slot[m] * I + r] = (_Float16)silu_mul(g, u);
+        }
+    }
+}
+
 // Shared gate/up (bf16 rows of H = 8*LPR*CPL).
 template <int LPR, int CPL, int MAXM, int NR>
 __device__ void shared_gateup(const FfnArgs &a, const Tokens<MAXM> &tk, int row0, float *__restrict__ hs) {
@@ -230,19 +323,23 @@ template <int MAXM> __device__ __forceinline__ void all_tokens(const FfnArgs &a,
     }
 }
 
-template <int LPR, int CPL, int SLPR, int SCPL, int MAXM, int NR>
+// FG: routed gate/up format (iq2x or q4k); LPR, CPL describe its routed rows.
+template <int FG, int LPR, int CPL, int SLPR, int SCPL, int MAXM, int NR>
 __global__ __launch_bounds__(256) void k_gemv_gateup(FfnArgs a, int wgs_per_expert, int n_routed_wgs,
                                                       _Float16 *__restrict__ h, float *__restrict__ hs) {
     __shared__ uint32_t cb4[256], sgn[128];
     const int bid = blockIdx.x;
     if (bid < n_routed_wgs) {
-        tables(a.codebook, cb4, sgn);
-        __syncthreads();
+        if constexpr (FG == FMT_IQ2X) {
+            tables(a.codebook, cb4, sgn);
+            __syncthreads();
+        }
         int e;
         Tokens<MAXM> tk;
         if (!routed_tokens<MAXM>(a, bid / wgs_per_expert, e, tk)) return;
         constexpr int ROWS = WAVES * NR * (64 / LPR);
-        routed_gateup<LPR, CPL, MAXM, NR>(a, e, tk, (bid % wgs_per_expert) * ROWS, cb4, sgn, h);
+        if constexpr (FG == FMT_Q4K) routed_gateup_q4k<LPR, CPL, MAXM, NR>(a, e, tk, (bid % wgs_per_expert) * ROWS, h);
+        else routed_gateup<LPR, CPL, MAXM, NR>(a, e, tk, (bid % wgs_per_expert) * ROWS, cb4, sgn, h);
     } else {
         Tokens<MAXM> tk;
         all_tokens<MAXM>(a, tk);
@@ -361,6 +458,92 @@ __device__ void routed_down(const FfnArgs &a, int e, const Tokens<MAXM> &tk, int
     }
 }
 
+// q4k chunk against fp16 h pairs: codes enter as fp16 1024 + q (pattern
+// 0x6400 | q), and  sum w h = d sc P - (1024 d sc + dmin m) S  per sub-block,
+// S the sum of its 32 h values.
+template <int MAXM>
+__device__ __forceinline__ void q4k_chunk_f16(uint4 q, uint4 meta, int j, const uint32_t (&hr)[MAXM][16],
+                                              const float (&hsum)[MAXM], float (&acc)[MAXM]) {
+    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+    float P[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) P[m] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f16x2_t t = __builtin_bit_cast(f16x2_t, ((qw[w] >> (4 * i)) & 0x000F000Fu) | 0x64006400u);
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) P[m] = dot2_f16(t, __builtin_bit_cast(f16x2_t, hr[m][4 * w + i]), P[m]);
+        }
+    const float sc = f16_bits_to_f32(meta.x & 0xFFFFu) * (float)q4k_field(meta.y, meta.z, meta.w, j);
+    const float off = __fmaf_rn(f16_bits_to_f32(meta.x >> 16), (float)q4k_field(meta.y, meta.z, meta.w, 8 + j),
+                                1024.f * sc);
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) acc[m] += __fmaf_rn(sc, P[m], -off * hsum[m]);
+}
+
+// Routed q4k down: rows of I = 32*LPR*CPL, a lane covers chunks cp + LPR*i.
+template <int LPR, int CPL, int MAXM, int NR>
+__device__ void routed_down_q4k(const FfnArgs &a, int e, const Tokens<MAXM> &tk, int row0,
+                                const _Float16 *__restrict__ h) {
+    constexpr int RPI = 64 / LPR;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int cp = lane % LPR, rsub = lane / LPR;
+    const int H = a.H, I = a.I;
+    const int64_t nb_row = I / MOE_QK, nb_mat = (int64_t)H * nb_row, NB = nb_mat * a.E;
+    uint32_t hr[CPL][MAXM][16];
+    float hsum[CPL][MAXM];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int ch = cp + LPR * i;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const int s = tk.slot[m < tk.n ? m : 0];
+            const uint4 *hp = reinterpret_cast<const uint4 *>(h + (int64_t)s * I + 32 * ch);
+            float sum = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint4 u = hp[v];
+                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    hr[i][m][4 * v + k] = w4[k];
+                    const f16x2_t p = __builtin_bit_cast(f16x2_t, w4[k]);
+                    sum += (float)p.x + (float)p.y;
+                }
+            }
+            hsum[i][m] = sum;
+        }
+    }
+    uint4 q[NR][CPL], mt[NR][CPL];
+#pragma unroll
+    for (int jr = 0; jr < NR; ++jr) {
+        const int r = min(row0 + (wv * NR + jr) * RPI + rsub, H - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int ch = cp + LPR * i;
+            const int64_t bl = (int64_t)e * nb_mat + (int64_t)r * nb_row + (ch >> 3);
+            q[jr][i] = *reinterpret_cast<const uint4 *>(a.down + bl * 128 + (ch & 7) * 16);
+            mt[jr][i] = *reinterpret_cast<const uint4 *>(a.down + NB * 128 + bl * 16);
+        }
+    }
+#pragma unroll
+    for (int jr = 0; jr < NR; ++jr) {
+        float acc[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) acc[m] = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) q4k_chunk_f16<MAXM>(q[jr][i], mt[jr][i], (cp + LPR * i) & 7, hr[i], hsum[i], acc);
+        const int r = row0 + (wv * NR + jr) * RPI + rsub;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const float o = row_sum<LPR>(acc[m]);
+            if (m < tk.n && cp == 0 && r < H) a.slot_out[(int64_t)tk.slot[m] * H + r] = o;
+        }
+    }
+}
+
 // Shared down: bf16 rows of Is = 8*LPR*CPL against fp32 h.
 template <int LPR, int CPL, int MAXM, int NR>
 __device__ void shared_down(const FfnArgs &a, const Tokens<MAXM> &tk, int row0, const float *__restrict__ hs) {
@@ -414,7 +597,8 @@ __device__ void shared_down(const FfnArgs &a, const Tokens<MAXM> &tk, int row0, 
     }
 }
 
-template <int LPR, int CPL, int SLPR, int SCPL, int MAXM, int NR>
+// FD: routed down format (q2k or q4k); LPR, CPL describe its routed rows.
+template <int FD, int LPR, int CPL, int SLPR, int SCPL, int MAXM, int NR>
 __global__ __launch_bounds__(256) void k_gemv_down(FfnArgs a, int wgs_per_expert, int n_routed_wgs,
                                                     const _Float16 *__restrict__ h, const float *__restrict__ hs) {
     const int bid = blockIdx.x;
@@ -423,7 +607,8 @@ __global__ __launch_bounds__(256) void k_gemv_down(FfnArgs a, int wgs_per_expert
         Tokens<MAXM> tk;
         if (!routed_tokens<MAXM>(a, bid / wgs_per_expert, e, tk)) return;
         constexpr int ROWS = WAVES * NR * (64 / LPR);
-        routed_down<LPR, CPL, MAXM, NR>(a, e, tk, (bid % wgs_per_expert) * ROWS, h);
+        if constexpr (FD == FMT_Q4K) routed_down_q4k<LPR, CPL, MAXM, NR>(a, e, tk, (bid % wgs_per_expert) * ROWS, h);
+        else routed_down<LPR, CPL, MAXM, NR>(a, e, tk, (bid % wgs_per_expert) * ROWS, h);
     } else {
         Tokens<MAXM> tk;
         all_tokens<MAXM>(a, tk);
@@ -452,7 +637,7 @@ bool split(int len, int per_chunk, int max_cpl, int &lpr, int &cpl) {
 
 constexpr int NR = 4;
 
-template <int MAXM, int LPR, int CPL, int SLPR, int SCPL>
+template <int FG, int MAXM, int LPR, int CPL, int SLPR, int SCPL>
 hipError_t run_gateup(const FfnArgs &a, int max_active, _Float16 *h, float *hs, hipStream_t st) {
     const int rows = WAVES * NR * (64 / LPR);
     const int wpe = (a.I + rows - 1) / rows;
@@ -462,12 +647,12 @@ hipError_t run_gateup(const FfnArgs &a, int max_active, _Float16 *h, float *hs, 
         const int srows = WAVES * shared_nr<SCPL>() * (64 / SLPR);
         ns = (a.Is + srows - 1) / srows;
     }
-    hipLaunchKernelGGL((k_gemv_gateup<LPR, CPL, SLPR, SCPL, MAXM, NR>), dim3(nr + ns), dim3(256), 0, st, a, wpe, nr, h,
-                       hs);
+    hipLaunchKernelGGL((k_gemv_gateup<FG, LPR, CPL, SLPR, SCPL, MAXM, NR>), dim3(nr + ns), dim3(256), 0, st, a, wpe, nr,
+                       h, hs);
     return hipGetLastError();
 }
 
-template <int MAXM, int LPR, int CPL, int SLPR, int SCPL>
+template <int FD, int MAXM, int LPR, int CPL, int SLPR, int SCPL>
 hipError_t run_down(const FfnArgs &a, int max_active, const _Float16 *h, const float *hs, hipStream_t st) {
     const int rows = WAVES * NR * (64 / LPR);
     const int wpe = (a.H + rows - 1) / rows;
@@ -477,8 +662,8 @@ hipError_t run_down(const FfnArgs &a, int max_active, const _Float16 *h, const f
         const int srows = WAVES * shared_nr<SCPL>() * (64 / SLPR);
         ns = (a.H + srows - 1) / srows;
     }
-    hipLaunchKernelGGL((k_gemv_down<LPR, CPL, SLPR, SCPL, MAXM, NR>), dim3(nr + ns), dim3(256), 0, st, a, wpe, nr, h,
-                       hs);
+    hipLaunchKernelGGL((k_gemv_down<FD, LPR, CPL, SLPR, SCPL, MAXM, NR>), dim3(nr + ns), dim3(256), 0, st, a, wpe, nr,
+                       h, hs);
     return hipGetLastError();
 }
 
@@ -487,24 +672,33 @@ hipError_t dispatch(const FfnArgs &a, _Float16 *h, float *hs, hipStream_t st) {
     const int max_active = min(a.T * a.k, a.E);
     hipError_t e = hipErrorInvalidValue;
     if (a.stages & STAGE_GATE_UP) {
-        // routed rows of H (64 per chunk), shared rows of H (8 per chunk)
-        if (a.H == 4096) e = run_gateup<MAXM, 64, 1, 64, 8>(a, max_active, h, hs, st);
-        else if (a.H == 2048) e = run_gateup<MAXM, 32, 1, 64, 4>(a, max_active, h, hs, st);
-        else if (a.H == 1024) e = run_gateup<MAXM, 16, 1, 64, 2>(a, max_active, h, hs, st);
-        else if (a.H == 512) e = run_gateup<MAXM, 8, 1, 64, 1>(a, max_active, h, hs, st);
+        // routed rows of H (iq2x: 64 weights per lane chunk, q4k: 32), shared rows of H (8 per chunk)
+#define MOE_GU(H_, LPR2_, CPL2_, LPR4_, CPL4_, SCPL_)                                                        \
+    if (a.H == H_) {                                                                                          \
+        if (a.fmt_gu == FMT_Q4K) e = run_gateup<FMT_Q4K, MAXM, LPR4_, CPL4_, 64, SCPL_>(a, max_active, h, hs, st); \
+        else e = run_gateup<FMT_IQ2X, MAXM, LPR2_, CPL2_, 64, SCPL_>(a, max_active, h, hs, st);             \
+    }
+        MOE_GU(4096, 64, 1, 64, 2, 8)
+        MOE_GU(2048, 32, 1, 64, 1, 4)
+        MOE_GU(1024, 16, 1, 32, 1, 2)
+        MOE_GU(512, 8, 1, 16, 1, 1)
+#undef MOE_GU
         if (e != hipSuccess) return e;
     }
     if (!(a.stages & STAGE_DOWN)) return hipSuccess;
-    // down: routed rows of I (64 per chunk), shared rows of Is (8 per chunk)
+    // down: routed rows of I (q2k: 64 weights per lane chunk, q4k: 32), shared rows of Is (8 per chunk)
     const int Is = a.Is > 0 ? a.Is : a.I;
-#define MOE_DOWN(I_, LPR_, SI_, SLPR_, SCPL_)                                                       \
-    if (a.I == I_ && Is == SI_) return run_down<MAXM, LPR_, 1, SLPR_, SCPL_>(a, max_active, h, hs, st);
-    MOE_DOWN(2048, 32, 2048, 64, 4)
-    MOE_DOWN(1024, 16, 1024, 64, 2)
-    MOE_DOWN(512, 8, 512, 64, 1)
-    MOE_DOWN(256, 4, 256, 32, 1)
-    MOE_DOWN(2048, 32, 1024, 64, 2)
-    MOE_DOWN(1024, 16, 2048, 64, 4)
+#define MOE_DOWN(I_, LPR2_, LPR4_, SI_, SLPR_, SCPL_)                                                         \
+    if (a.I == I_ && Is == SI_) {                                                                             \
+        if (a.fmt_d == FMT_Q4K) return run_down<FMT_Q4K, MAXM, LPR4_, 1, SLPR_, SCPL_>(a, max_active, h, hs, st); \
+        return run_down<FMT_Q2K, MAXM, LPR2_, 1, SLPR_, SCPL_>(a, max_active, h, hs, st);                   \
+    }
+    MOE_DOWN(2048, 32, 64, 2048, 64, 4)
+    MOE_DOWN(1024, 16, 32, 1024, 64, 2)
+    MOE_DOWN(512, 8, 16, 512, 64, 1)
+    MOE_DOWN(256, 4, 8, 256, 32, 1)
+    MOE_DOWN(2048, 32, 64, 1024, 64, 2)
+    MOE_DOWN(1024, 16, 32, 2048, 64, 4)
 #undef MOE_DOWN
     return hipErrorInvalidValue;
 }
@@ -514,7 +708,9 @@ hipError_t dispatch(const FfnArgs &a, _Float16 *h, float *hs, hipStream_t st) {
 namespace moe {
 
 bool ffn_gemv_supported(const FfnArgs &a) {
-    if (!a.x_bf16 || a.fmt_gu != FMT_IQ2X || a.fmt_d != FMT_Q2K || a.T > 4) return false;
+    if (!a.x_bf16 || a.T > 4) return false;
+    if (a.fmt_gu != FMT_IQ2X && a.fmt_gu != FMT_Q4K) return false;
+    if (a.fmt_d != FMT_Q2K && a.fmt_d != FMT_Q4K) return false;
     if (!(a.H == 4096 || a.H == 2048 || a.H == 1024 || a.H == 512)) return false;
     const int Is = a.Is > 0 ? a.Is : a.I;
     const int pairs[6][2] = {{2048, 2048}, {1024, 1024}, {512, 512}, {256, 256}, {2048, 1024}, {1024, 2048}};

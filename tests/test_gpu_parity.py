@@ -209,7 +209,8 @@ LAYER_CASES = [
     ("small", 5, 0), ("small", 37, 0), ("small", 1, 3), ("small", 3, 3), ("mid", 70, 0), ("mid", 130, 0),
     ("mid", 300, 0),
     # q4k routed experts (4.5 bpw) and mixed formats: decode sizes and grouped GEMM
-    ("small_q4k", 1, 0), ("small_q4k", 3, 0), ("small_q4k", 37, 0), ("small_q4k", 3, 3), ("small_q4k", 70, 0),
+    ("small_q4k", 1, 0), ("small_q4k", 3, 0), ("small_q4k", 4, 0), ("small_q4k", 3, 1), ("small_q4k", 37, 0),
+    ("small_q4k", 3, 3), ("small_q4k", 70, 0),
     ("small_mix_a", 2, 0), ("small_mix_a", 37, 0), ("small_mix_b", 2, 0), ("small_mix_b", 37, 0),
 ]
 
@@ -231,15 +232,16 @@ def test_layer_matches_oracle(m, name, T, path):
     assert err.max() <= TOL
 
 
-@pytest.mark.parametrize("T", [1, 3])
-def test_decode_layer_full_size(m, T):
+@pytest.mark.parametrize("name,T", [("decode", 1), ("decode", 3), ("long_q4k", 1), ("long_q4k", 3)])
+def test_decode_layer_full_size(m, name, T):
     """Full-size decode layer (hidden 4096, 256 experts, top-8, intermediate
-    2048, bf16 shared expert) on several independent calls."""
-    L = _layer("decode")
+    2048, bf16 shared expert), 2-bit or q4k routed experts, on several
+    independent calls of 1 or 3 tokens."""
+    L = _layer(name)
     sp = L.spec
     xs = synth.activations("decode", 4 * T, sp.hidden, True, seed=901 + T)
     for c in range(4):
-        note(f"decode full size T={T} call {c}")
+        note(f"decode full size {name} T={T} call {c}")
         x = xs[c * T:(c + 1) * T]
         got = _run_layer(m, L, x, 0)
         ref = _oracle_layer(L, x)
