@@ -49,7 +49,57 @@ def parse():
     p.add_argument("--prefill-reps", type=int, default=5)
     p.add_argument("--no-q4k", action="store_true", help="skip the 4-bit (q4k) routed-expert workloads")
     p.add_argument("--verify-steps", type=int, default=334, help="steps of the 3-token verify micro-batch")
+    p.add_argument("--probe", action="store_true",
+                   help="hardware-counter probe: --kernel-reps eager launches of the decode gate/up kernel over "
+                        "cycled layer copies, then one 1 GiB device-to-device copy (the reference for scaling "
+                        "the traffic counters); prints one JSON line")
     return p.parse_args()
+
+
+# HBM traffic of one decode gate/up launch, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE counters on that kernel, each scaled by the same counter's reading
+# for a 1 GiB device-to-device copy in the same process.  Valid only for the
+# kernel source it was measured on (sha256 of csrc/ffn_gemv.hip).
+GATEUP_TRAFFIC = {"src_sha256": "e5c9af9b907132af1020cb92b7c65bd3bdc1e20b9dde66522b95774625e1feb3", "bytes": 68522366}
+
+
+def gemv_source_sha():
+    import hashlib
+    with open(os.path.join(ROOT, "bit_quantized_moe_permute_amd", "csrc", "ffn_gemv.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def probe(args):
+    """Eager launches only, for counter collection (no timing)."""
+    import torch
+
+    import synth
+    from bit_quantized_moe_permute_amd import moe_expert_gate_up, moe_route
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers
+
+    dev = torch.device("cuda:0")
+    sp = synth.SPECS["decode"]
+    H, E, k = sp.hidden, sp.n_experts, sp.top_k
+    L = synth.make_layer(sp)
+    layers = [DeviceLayer.from_synth(L, device=dev)]
+    for _ in range(args.layers - 1):
+        layers.append(layers[0].clone())
+    x_np = synth.activations("decode", synth.TOKENS["decode"], H, True)
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    reps = args.kernel_reps or 50
+    b = LayerBuffers.allocate(layers[0], 1)
+    for i in range(reps):
+        Li = layers[i % args.layers]
+        xi = x[i: i + 1]
+        moe_route(xi, Li.w_router, E, k, b.topk_idx, b.topk_w, b.offsets, b.perm, b.active, b.ws_route)
+        moe_expert_gate_up(Li.desc, xi, b.topk_idx, b.offsets, b.perm, b.active, b.ws_ffn)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "decode gate/up", "launches": reps, "copy_bytes": 1 << 30,
+                      "gemv_src_sha256": gemv_source_sha()}), flush=True)
 
 
 def graph_steps(step, K, W):
@@ -108,6 +158,10 @@ def main():
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the layer is a single-GPU hot path "
                                    "(multi-GPU expert parallelism is described, not built)", "n_gpus": args.gpus}))
         sys.exit(2)
+
+    if args.probe:
+        probe(args)
+        return
 
     import torch
 
@@ -200,8 +254,9 @@ def main():
     achieved = nbytes["gate_up"] / (gu_us * 1e-6) / 1e9
     log(f"gate/up kernel: {gu_us:.2f} us/launch, {achieved:.0f} GB/s algorithmic")
 
+    traffic = GATEUP_TRAFFIC["bytes"] if GATEUP_TRAFFIC["src_sha256"] == gemv_source_sha() else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "k_gemv_gateup (routed iq2x gate/up + bf16 shared gate/up, fused SwiGLU)",
                 "bytes_per_launch": nbytes["gate_up"], "avg_launch_us": round(gu_us, 3)}
     step_bw = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
