@@ -211,6 +211,145 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t *__restrict__ to
     }
 }
 
+// ---------------------------------------------------------------------------
+// Small batches (T <= 4: decode and verify).  Two launches instead of three.
+// ---------------------------------------------------------------------------
+constexpr int SMALL_T = 4;
+
+// One wave per (expert, token), grid (E/4, T).  Lane p holds partial p and
+// issues all its H/64 loads before the first multiply, so the latency of the
+// strided loads is paid once; the sum order is the same as k_router_logits.
+template <bool XB, bool WB, int NJ>
+__global__ __launch_bounds__(256) void k_router_logits_small(const void *__restrict__ x, const void *__restrict__ w,
+                                                             const float *__restrict__ bias, int E,
+                                                             float *__restrict__ logits,
+                                                             float *__restrict__ logits_copy) {
+    constexpr int H = 64 * NJ;
+    const int lane = threadIdx.x & 63, e = blockIdx.x * 4 + (threadIdx.x >> 6), t = blockIdx.y;
+    if (e >= E) return;
+    float wv[NJ], xv[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        wv[j] = (float)ld<WB>(w, (int64_t)e * H + lane + 64 * j);
+        xv[j] = (float)ld<XB>(x, (int64_t)t * H + lane + 64 * j);
+    }
+    double v = 0.0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) v = __fma_rn((double)wv[j], (double)xv[j], v);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v = v + __shfl_down(v, s, 64);
+    if (lane == 0) {
+        float l = (float)v;
+        if (bias) l = (float)((double)l + (double)bias[e]);
+        logits[(int64_t)t * E + e] = l;
+        if (logits_copy) logits_copy[(int64_t)t * E + e] = l;
+    }
+}
+
+// Top-k, weights and permutation for T <= 4 tokens in one workgroup of 1024
+// threads.  Expert e of token t carries the key (orderable logit bits, then
+// 255 - e): a larger key is a larger logit, ties going to the lower index, and
+// keys are distinct.  The rank of e is the number of larger keys, counted in
+// four quarters by four threads and summed; ranks below k are the selection,
+// already in order.  Slot s = t*k + j then goes to position offsets[e] + (the
+// number of earlier slots with the same expert).
+__global__ __launch_bounds__(1024) void k_select_small(const float *__restrict__ logits, int T, int E, int k,
+                                                       int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+                                                       int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+                                                       int32_t *__restrict__ active) {
+    __shared__ float lg[SMALL_T][256];
+    __shared__ __attribute__((aligned(16))) unsigned long long key[SMALL_T][256];
+    __shared__ int part[4][SMALL_T][256];
+    __shared__ int sel[SMALL_T * 256];
+    __shared__ double ex[SMALL_T][256];
+    __shared__ int cnt[256];
+    const int tid = threadIdx.x, e = tid & 255, q = tid >> 8;
+    if (q < T) {
+        const float l = e < E ? logits[q * E + e] : 0.f;
+        lg[q][e] = l;
+        const uint32_t u = __float_as_uint(l + 0.0f);                       // -0 compares equal to +0
+        const uint32_t ord = u ^ ((u >> 31) ? 0xFFFFFFFFu : 0x80000000u);
+        key[q][e] = e < E ? (((unsigned long long)ord << 32) | (uint32_t)(255 - e)) : 0ull;
+    }
+    __syncthreads();
+    for (int t = 0; t < T; ++t) {
+        const unsigned long long me = key[t][e];
+        const ulonglong2 *row = reinterpret_cast<const ulonglong2 *>(&key[t][64 * q]);
+        int r = 0;
+#pragma unroll
+        for (int o2 = 0; o2 < 32; ++o2) {
+            const ulonglong2 u = row[o2];
+            r += (u.x > me ? 1 : 0) + (u.y > me ? 1 : 0);
+        }
+        part[q][t][e] = r;
+    }
+    __syncthreads();
+    if (q < T && e < E) {
+        const int r = part[0][q][e] + part[1][q][e] + part[2][q][e] + part[3][q][e];
+        if (r < k) sel[q * k + r] = e;
+    }
+    __syncthreads();
+    const int S = T * k;
+    // softmax over the selected logits, binary64
+    for (int s = tid; s < S; s += 1024) {
+        const int t = s / k;
+        ex[t][s % k] = exp((double)lg[t][sel[s]] - (double)lg[t][sel[t * k]]);
+    }
+    if (tid < E) {
+        int c = 0;
+        for (int s = 0; s < S; ++s) c += sel[s] == tid ? 1 : 0;
+        cnt[tid] = c;
+    }
+    __syncthreads();
+    for (int s = tid; s < S; s += 1024) {
+        const int t = s / k;
+        double den = 0.0;
+        for (int j = 0; j < k; ++j) den += ex[t][j];
+        topk_idx[s] = sel[s];
+        topk_w[s] = (float)(ex[t][s % k] / den);
+    }
+    // offsets and the active list: exclusive scans over the experts (one wave)
+    if (tid < 64) {
+        int c[4], a[4], cs = 0, as = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int x = 4 * tid + i;
+            c[i] = x < E ? cnt[x] : 0;
+            a[i] = c[i] > 0;
+            cs += c[i];
+            as += a[i];
+        }
+        int ci = cs, ai = as;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(ci, o, 64), v = __shfl_up(ai, o, 64);
+            if (tid >= o) { ci += u; ai += v; }
+        }
+        int cpre = ci - cs, apre = ai - as;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int x = 4 * tid + i;
+            if (x < E) {
+                offsets[x] = cpre;
+                cnt[x] = cpre;                   // becomes the expert's base position
+                if (a[i]) active[1 + apre] = x;
+            }
+            cpre += c[i];
+            apre += a[i];
+        }
+        if (tid == 63) {
+            offsets[E] = ci;
+            active[0] = ai;
+        }
+    }
+    __syncthreads();
+    for (int s = tid; s < S; s += 1024) {
+        const int x = sel[s];
+        int before = 0;
+        for (int o = 0; o < s; ++o) before += sel[o] == x ? 1 : 0;
+        perm[cnt[x] + before] = s;
+    }
+}
+
 template <bool XB, bool WB>
 hipError_t launch_logits(const RouteArgs &a, hipStream_t st) {
     if (a.T == 1) {
@@ -233,8 +372,40 @@ hipError_t launch_logits(const RouteArgs &a, hipStream_t st) {
 
 namespace moe {
 
+template <bool XB, bool WB>
+hipError_t launch_logits_small(const RouteArgs &a, hipStream_t st) {
+    const dim3 grd((a.E + 3) / 4, a.T);
+#define MOE_LOGITS(NJ_)                                                                                      \
+    case 64 * NJ_:                                                                                           \
+        hipLaunchKernelGGL((k_router_logits_small<XB, WB, NJ_>), grd, dim3(256), 0, st, a.x, a.w, a.bias, a.E, \
+                           a.logits_ws, a.logits_out);                                                       \
+        break;
+    switch (a.H) {
+        MOE_LOGITS(64)
+        MOE_LOGITS(32)
+        MOE_LOGITS(16)
+        MOE_LOGITS(8)
+        MOE_LOGITS(4)
+        default: return hipErrorInvalidValue;
+    }
+#undef MOE_LOGITS
+    return hipGetLastError();
+}
+
+bool small_logits_shape(int H) { return H == 4096 || H == 2048 || H == 1024 || H == 512 || H == 256; }
+
 hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
     hipError_t e;
+    if (a.T <= SMALL_T && small_logits_shape(a.H)) {
+        if (a.x_bf16 && a.w_bf16) e = launch_logits_small<true, true>(a, st);
+        else if (a.x_bf16) e = launch_logits_small<true, false>(a, st);
+        else if (a.w_bf16) e = launch_logits_small<false, true>(a, st);
+        else e = launch_logits_small<false, false>(a, st);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_select_small, dim3(1), dim3(1024), 0, st, a.logits_ws, a.T, a.E, a.k, a.topk_idx, a.topk_w,
+                           a.offsets, a.perm, a.active);
+        return hipGetLastError();
+    }
     if (a.x_bf16 && a.w_bf16) e = launch_logits<true, true>(a, st);
     else if (a.x_bf16) e = launch_logits<true, false>(a, st);
     else if (a.w_bf16) e = launch_logits<false, true>(a, st);

@@ -136,33 +136,50 @@ def test_route_matches_oracle(m, name, T):
 
 
 @pytest.mark.parametrize("k", [1, 16])
-def test_route_k_extremes(m, k):
-    note(f"route k={k}")
+@pytest.mark.parametrize("T", [1, 4, 9])
+def test_route_k_extremes(m, k, T):
+    note(f"route k={k} T={T}")
     wr, _ = synth.make_router("small")
-    x = synth.activations("small", 9, 512, True)
+    x = synth.activations("small", T, 512, True)
     _check_route(m, x, wr, 16, k)
 
 
-def test_route_zero_input_ties(m):
-    note("route zero input")
+@pytest.mark.parametrize("T", [1, 3, 5])
+def test_route_zero_input_ties(m, T):
+    note(f"route zero input T={T}")
     wr, _ = synth.make_router("small")
-    x = np.zeros((5, 512), np.uint16)
+    x = np.zeros((T, 512), np.uint16)
     _, idx, tw, _, _, _ = _route_gpu(m, x, wr, 16, 4)
-    assert np.array_equal(idx, np.tile(np.arange(4), (5, 1)))
-    assert np.array_equal(tw, np.full((5, 4), 0.25, np.float32))
+    assert np.array_equal(idx, np.tile(np.arange(4), (T, 1)))
+    assert np.array_equal(tw, np.full((T, 4), 0.25, np.float32))
+
+
+def test_route_full_size_decode_tokens(m):
+    """The decode router (4096 x 256, bf16) on 64 separate one-token calls and 16 three-token calls."""
+    sp = synth.SPECS["decode"]
+    wr, _ = synth.make_router(sp)
+    x = synth.activations("decode", 112, sp.hidden, True, seed=977)
+    for i in range(64):
+        _check_route(m, x[i:i + 1], wr, sp.n_experts, sp.top_k)
+    for i in range(16):
+        _check_route(m, x[64 + 3 * i: 67 + 3 * i], wr, sp.n_experts, sp.top_k)
+    note("route decode tokens: 64 x T=1, 16 x T=3")
 
 
 def test_route_summation_order_golden(m):
     """tests/golden/router_order.txt: cancellation cases where the fixed order decides the logit."""
     from test_oracle_layer import _router_order_cases
     for name, H, entries, want in _router_order_cases():
-        note(f"route order {name}")
-        x = np.ones((1, H), np.float32)
-        w = np.zeros((2, H), np.float32)
-        for h, v in entries:
-            w[0, h] = v
-        lg, _, _, _, _, _ = _route_gpu(m, x, w, 2, 1)
-        assert lg[0, 0] == np.float32(want), (name, lg[0, 0])
+        # also zero-padded to 256 columns (padding adds exact zeros to the partials), which takes the
+        # small-batch router kernel
+        for Hp in (H, 256):
+            note(f"route order {name} H={Hp}")
+            x = np.ones((1, Hp), np.float32)
+            w = np.zeros((2, Hp), np.float32)
+            for h, v in entries:
+                w[0, h] = v
+            lg, _, _, _, _, _ = _route_gpu(m, x, w, 2, 1)
+            assert lg[0, 0] == np.float32(want), (name, Hp, lg[0, 0])
 
 
 # ----------------------------------------------------------------------------
