@@ -257,7 +257,7 @@ def main():
     traffic = GATEUP_TRAFFIC["bytes"] if GATEUP_TRAFFIC["src_sha256"] == gemv_source_sha() else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_gemv_gateup (routed iq2x gate/up + bf16 shared gate/up, fused SwiGLU)",
+                "kernel": "k_gemv_gateup_mfma (routed iq2x gate/up on fp8 MFMA + bf16 shared gate/up, fused SwiGLU)",
                 "bytes_per_launch": nbytes["gate_up"], "avg_launch_us": round(gu_us, 3)}
     step_bw = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
 

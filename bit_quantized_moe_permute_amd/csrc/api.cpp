@@ -148,6 +148,8 @@ static moe_status check_layer(const moe_layer_desc *L, const char *fn) {
     if (!aligned(L->gate, 16) || !aligned(L->up, 16) || !aligned(L->down, 16))
         return fail(MOE_ERR_INVALID_ARG, "%s: expert weights not 16-byte aligned", fn);
     if (L->gate_up_fmt == MOE_FMT_IQ2X && !L->codebook) return fail(MOE_ERR_INVALID_ARG, "%s: null codebook", fn);
+    if (L->gate_up_fmt == MOE_FMT_IQ2X && !aligned(L->codebook, 8))
+        return fail(MOE_ERR_INVALID_ARG, "%s: codebook not 8-byte aligned", fn);
     if (L->shared_inter < 0) return fail(MOE_ERR_INVALID_ARG, "%s: shared_inter < 0", fn);
     if (L->shared_inter > 0) {
         if (!L->shared_gate || !L->shared_up || !L->shared_down)

@@ -323,6 +323,263 @@ template <int MAXM> __device__ __forceinline__ void all_tokens(const FfnArgs &a,
     }
 }
 
+// ---------------------------------------------------------------------------
+// iq2x gate/up on the matrix cores (T <= 4 tokens per expert).
+//
+// v_mfma_f32_16x16x32_fp8_fp8 with the weights as B (32 K x 16 rows) and the
+// activations as A.  Codebook magnitudes 1, 2, 3 and their signs are exact in
+// fp8 (e4m3), so an 8-weight sub-group is two LDS lookups (codebook row as
+// eight fp8 bytes, sign byte spread to the 0x80 bits) and an OR: no
+// conversion.  Activations are split into two e4m3 pieces per 32-value group,
+// hi = e4m3(x') and lo = e4m3(x' - hi) with x' = x * 2^s, 2^s the power of two
+// that brings the group's max|x| into [128, 256); for |x'| >= 2^-2 the two
+// pieces hold all eight significant bits of the bf16 value, and the group's
+// sums pick up 2^-s with the weight scales.
+//
+// Lane (n, q) (n = lane % 16, q = lane / 16) decodes row n; in every
+// 256-weight block quarter q takes 16-byte chunk q (groups q and q + 4), so a
+// lane owns whole groups and their 4-bit scales.  The pieces of token t sit in
+// A rows 4q + 2t + p (p: 0 hi, 1 lo, t < 2 per product), non-zero only in the K
+// quarter q: quarter q's products land in D rows 4q .. 4q+3, which the lanes
+// of quarter q hold.  A group is 4 K-steps into a fresh accumulator, then
+// added to the lane's running sums times (2s+1) * d * 2^-s(x).
+// A workgroup of H/512 waves takes one expert and MF_RB*16 rows, wave w the
+// K slice [512w, 512w+512); the slices and quarters are summed in LDS.
+// ---------------------------------------------------------------------------
+constexpr int MF_KW = 512;
+constexpr int MF_RB = 4;
+constexpr int MF_MAXH = 4096;
+
+// index: sign byte of a prepared field (7 signs, bit 7 belongs to the group scale)
+__device__ __forceinline__ uint64_t sign_fp8(int b) {
+    const uint32_t s7 = (uint32_t)b & 0x7Fu;
+    const uint32_t bits = s7 | ((__builtin_popcount(s7) & 1u) << 7);
+    uint64_t r = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r |= (uint64_t)((bits >> j) & 1u) << (8 * j + 7);
+    return r;
+}
+
+typedef __attribute__((ext_vector_type(4))) float mf_acc_t;
+
+__device__ __forceinline__ mf_acc_t mfma_fp8(uint64_t a, uint64_t b, mf_acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)a, (long)b, c, 0, 0, 0);
+}
+
+// active, offsets, perm: the routing arrays, read-only here; with uniform
+// indices they are read through the scalar cache, whose wait counter is
+// separate from the weight loads in flight.
+template <int MAXM>
+__device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32_t *__restrict__ active,
+                                                   const int32_t *__restrict__ offsets,
+                                                   const int32_t *__restrict__ perm, int ai, int row0,
+                                                   _Float16 *__restrict__ h, uint64_t *cb8, uint64_t *sg8,
+                                                   uint8_t (*xq)[2][MF_MAXH], float (*xsc)[MF_MAXH / 32], float *red) {
+    constexpr int NP = (MAXM + 1) / 2;                       // products per K-step (two tokens each)
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
+    const int n = lane & 15, qd = lane >> 4;
+    const int H = a.H, I = a.I;
+    const int k0w = wv * MF_KW;
+    // --- expert id (scalar), codebook rows and activations first: their loads
+    // complete before the weights' in issue order
+    const int n_active = active[0];
+    const int e = min(max(active[1 + ai], 0), a.E - 1);      // in range even for an idle workgroup
+    uint2 cbrow[4];                                          // rows tid + i * blockDim (blockDim >= 64)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = tid + i * (int)blockDim.x;
+        cbrow[i] = r < 256 ? reinterpret_cast<const uint2 *>(a.codebook)[r] : make_uint2(0u, 0u);
+    }
+    uint4 xv[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m)
+        if (m < a.T)
+            xv[m] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + (int64_t)m * H + 8 * tid);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = tid + i * (int)blockDim.x;
+        if (row < 256) {
+            uint64_t r = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t mag = ((j < 4 ? cbrow[i].x : cbrow[i].y) >> (8 * (j & 3))) & 0xFFu;   // 1, 2 or 3
+                r |= (uint64_t)(mag == 1 ? 0x38u : (mag == 2 ? 0x40u : 0x44u)) << (8 * j);
+            }
+            cb8[row] = r;
+            sg8[row] = sign_fp8(row);
+        }
+    }
+    // --- all weights of this wave: units u = (row block u / 2, K block u % 2)
+    const int64_t nb_row = H / MOE_QK, nb_mat = (int64_t)I * nb_row, NB = nb_mat * a.E;
+    uint4 wq[2 * MF_RB][2];                                  // [unit][matrix]: chunk qd of the block
+    uint32_t wd[2 * MF_RB];                                   // fp16 block scales of gate | up << 16
+#pragma unroll
+    for (int u = 0; u < 2 * MF_RB; ++u) {
+        const int r = min(row0 + 16 * (u >> 1) + n, I - 1);
+        const int64_t bl = (int64_t)e * nb_mat + (int64_t)r * nb_row + (k0w >> 8) + (u & 1);
+        wq[u][0] = reinterpret_cast<const uint4 *>(a.gate + bl * 64)[qd];
+        wq[u][1] = reinterpret_cast<const uint4 *>(a.up + bl * 64)[qd];
+        wd[u] = (uint32_t)reinterpret_cast<const uint16_t *>(a.gate + NB * 64)[bl] |
+                ((uint32_t)reinterpret_cast<const uint16_t *>(a.up + NB * 64)[bl] << 16);
+    }
+    // --- activation pieces of every token of the call: thread tid converts
+    // x[t][8 tid .. 8 tid + 7]; the four threads of a 32-value group share 2^s
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        if (m >= a.T) break;
+        const uint32_t w4[4] = {xv[m].x, xv[m].y, xv[m].z, xv[m].w};
+        float mx = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(w4[k] << 16)), fabsf(__uint_as_float(w4[k] & 0xFFFF0000u))));
+        mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+        const int sh = mx > 0.f ? 7 - ilogbf(mx) : 0;
+        if ((tid & 3) == 0) xsc[m][tid >> 2] = ldexpf(1.f, -sh);
+        uint32_t hi2[2], lo2[2];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float v0 = ldexpf(__uint_as_float(w4[k] << 16), sh);
+            const float v1 = ldexpf(__uint_as_float(w4[k] & 0xFFFF0000u), sh);
+            const uint32_t hp = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+            const float r0 = v0 - __builtin_amdgcn_cvt_f32_fp8(hp, 0);
+            const float r1 = v1 - __builtin_amdgcn_cvt_f32_fp8(hp, 1);
+            const uint32_t lp = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+            if (k & 1) { hi2[k >> 1] |= (hp & 0xFFFFu) << 16; lo2[k >> 1] |= (lp & 0xFFFFu) << 16; }
+            else { hi2[k >> 1] = hp & 0xFFFFu; lo2[k >> 1] = lp & 0xFFFFu; }
+        }
+        *reinterpret_cast<uint2 *>(&xq[m][0][8 * tid]) = make_uint2(hi2[0], hi2[1]);
+        *reinterpret_cast<uint2 *>(&xq[m][1][8 * tid]) = make_uint2(lo2[0], lo2[1]);
+    }
+    if (ai >= n_active) return;                               // whole workgroup: fewer experts than launched
+    // --- the expert's tokens (slot t*k + j in the permutation)
+    Tokens<MAXM> tk;
+    {
+        const int o0 = offsets[e];
+        tk.n = min(offsets[e + 1] - o0, MAXM);
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const int sl = perm[o0 + (m < tk.n ? m : 0)];
+            tk.slot[m] = sl;
+            tk.tok[m] = min(sl / a.k, MAXM - 1);
+        }
+    }
+    __syncthreads();
+    // --- A operand of this lane: A row n = 4 qa + 2 t + p holds slot (2 pr + t), piece p, in K quarter qa
+    const bool arow = (n >> 2) == qd;
+    const int at0 = (n >> 1) & 1, ap = n & 1;
+    int axt[NP];
+    bool aval[NP];
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+        const int sl = 2 * pr + at0;
+        aval[pr] = arow && sl < tk.n;
+        int tt = 0;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m)
+            if (m == sl) tt = tk.tok[m];
+        axt[pr] = tt;
+    }
+    const mf_acc_t zero = {};
+    float tot[2][MAXM];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) tot[f][m] = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2 * MF_RB; ++u) {
+        const int b = u & 1;
+        const float dsc[2] = {f16_bits_to_f32(wd[u] & 0xFFFFu), f16_bits_to_f32(wd[u] >> 16)};
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {                              // group qd + 4 gi of the block
+            const int kg = k0w + 256 * b + 32 * (qd + 4 * gi);       // first column of the group
+            mf_acc_t acc[2][NP];
+#pragma unroll
+            for (int ps = 0; ps < 4; ++ps) {
+                uint64_t A[NP];
+#pragma unroll
+                for (int pr = 0; pr < NP; ++pr)
+                    A[pr] = aval[pr] ? *reinterpret_cast<const uint64_t *>(&xq[axt[pr]][ap][kg + 8 * ps]) : 0ull;
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    const uint4 c = wq[u][f];
+                    const uint32_t dw = gi ? ((ps >> 1) ? c.w : c.z) : ((ps >> 1) ? c.y : c.x);
+                    const uint32_t fld = (ps & 1) ? (dw >> 16) : (dw & 0xFFFFu);
+                    const uint64_t wb = cb8[fld & 0xFFu] | sg8[fld >> 8];
+#pragma unroll
+                    for (int pr = 0; pr < NP; ++pr) acc[f][pr] = mfma_fp8(A[pr], wb, ps == 0 ? zero : acc[f][pr]);
+                }
+            }
+            float xs[MAXM];
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) xs[m] = xsc[tk.tok[m]][kg >> 5];
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                const uint4 c = wq[u][f];
+                const uint32_t lo = gi ? c.z : c.x, hi = gi ? c.w : c.y;
+                const uint32_t sg = ((lo >> 15) & 1u) | ((lo >> 30) & 2u) | ((hi >> 13) & 4u) | ((hi >> 28) & 8u);
+                const float S = dsc[f] * (float)(2u * sg + 1u);
+#pragma unroll
+                for (int m = 0; m < MAXM; ++m) {
+                    const mf_acc_t &d = acc[f][m >> 1];
+                    const float v = (m & 1) ? d[2] + d[3] : d[0] + d[1];
+                    tot[f][m] = __fmaf_rn(S * xs[m], v, tot[f][m]);
+                }
+            }
+        }
+        if (b == 1) {                                                 // row block done: sum the quarters, to LDS
+            const int rb = u >> 1;
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int m = 0; m < MAXM; ++m) {
+                    float v = tot[f][m];
+                    v += __shfl_xor(v, 16, 64);
+                    v += __shfl_xor(v, 32, 64);
+                    if (qd == 0) red[(((wv * MF_RB + rb) * 2 + f) * MAXM + m) * 16 + n] = v;
+                    tot[f][m] = 0.f;
+                }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < MF_RB * MAXM * 16; i += blockDim.x) {
+        const int nn = i & 15, m = (i >> 4) % MAXM, rb = (i >> 4) / MAXM;
+        const int r = row0 + 16 * rb + nn;
+        if (m >= tk.n || r >= I) continue;
+        float g = 0.f, u = 0.f;
+        for (int w = 0; w < nw; ++w) {
+            g += red[(((w * MF_RB + rb) * 2 + 0) * MAXM + m) * 16 + nn];
+            u += red[(((w * MF_RB + rb) * 2 + 1) * MAXM + m) * 16 + nn];
+        }
+        h[(int64_t)tk.slot[m] * I + r] = (_Float16)silu_mul(g, u);
+    }
+}
+
+// Routed iq2x rows on the matrix cores, shared bf16 rows as in k_gemv_gateup.
+template <int SLPR, int SCPL, int MAXM>
+__global__ __launch_bounds__(512) void k_gemv_gateup_mfma(FfnArgs a, const int32_t *__restrict__ active,
+                                                           const int32_t *__restrict__ offsets,
+                                                           const int32_t *__restrict__ perm, int wgs_per_expert,
+                                                           int n_routed_wgs, _Float16 *__restrict__ h,
+                                                           float *__restrict__ hs) {
+    __shared__ uint64_t cb8[256], sg8[256];
+    __shared__ __attribute__((aligned(16))) uint8_t xq[MAXM][2][MF_MAXH];
+    __shared__ float xsc[MAXM][MF_MAXH / 32];
+    __shared__ float red[(MF_MAXH / MF_KW) * MF_RB * 2 * MAXM * 16];
+    const int bid = blockIdx.x;
+    if (bid < n_routed_wgs) {
+        const int ai = bid / wgs_per_expert;
+        routed_gateup_mfma<MAXM>(a, active, offsets, perm, ai, (bid % wgs_per_expert) * (16 * MF_RB), h, cb8, sg8,
+                                 xq, xsc, red);
+    } else {
+        Tokens<MAXM> tk;
+        all_tokens<MAXM>(a, tk);
+        constexpr int SNR = shared_nr<SCPL>();
+        const int rows = (int)(blockDim.x >> 6) * SNR * (64 / SLPR);
+        shared_gateup<SLPR, SCPL, MAXM, SNR>(a, tk, (bid - n_routed_wgs) * rows, hs);
+    }
+}
+
 // FG: routed gate/up format (iq2x or q4k); LPR, CPL describe its routed rows.
 template <int FG, int LPR, int CPL, int SLPR, int SCPL, int MAXM, int NR>
 __global__ __launch_bounds__(256) void k_gemv_gateup(FfnArgs a, int wgs_per_expert, int n_routed_wgs,
@@ -652,6 +909,25 @@ hipError_t run_gateup(const FfnArgs &a, int max_active, _Float16 *h, float *hs, 
     return hipGetLastError();
 }
 
+template <int MAXM, int SLPR, int SCPL>
+hipError_t run_gateup_mfma(const FfnArgs &a, int max_active, _Float16 *h, float *hs, hipStream_t st) {
+    const int threads = a.H / 8;                                  // H/512 waves
+    const int wpe = a.I / (16 * MF_RB);
+    const int nr = max_active * wpe;
+    int ns = 0;
+    if (a.Is > 0) {
+        const int srows = (threads / 64) * shared_nr<SCPL>() * (64 / SLPR);
+        ns = (a.Is + srows - 1) / srows;
+    }
+    hipLaunchKernelGGL((k_gemv_gateup_mfma<SLPR, SCPL, MAXM>), dim3(nr + ns), dim3(threads), 0, st, a, a.active,
+                       a.offsets, a.perm, wpe, nr, h, hs);
+    return hipGetLastError();
+}
+
+bool gateup_mfma_ok(const FfnArgs &a) {
+    return a.fmt_gu == FMT_IQ2X && a.H % MF_KW == 0 && a.H >= MF_KW && a.H <= MF_MAXH && a.I % (16 * MF_RB) == 0;
+}
+
 template <int FD, int MAXM, int LPR, int CPL, int SLPR, int SCPL>
 hipError_t run_down(const FfnArgs &a, int max_active, const _Float16 *h, const float *hs, hipStream_t st) {
     const int rows = WAVES * NR * (64 / LPR);
@@ -676,6 +952,7 @@ hipError_t dispatch(const FfnArgs &a, _Float16 *h, float *hs, hipStream_t st) {
 #define MOE_GU(H_, LPR2_, CPL2_, LPR4_, CPL4_, SCPL_)                                                        \
     if (a.H == H_) {                                                                                          \
         if (a.fmt_gu == FMT_Q4K) e = run_gateup<FMT_Q4K, MAXM, LPR4_, CPL4_, 64, SCPL_>(a, max_active, h, hs, st); \
+        else if (gateup_mfma_ok(a)) e = run_gateup_mfma<MAXM, 64, SCPL_>(a, max_active, h, hs, st);          \
         else e = run_gateup<FMT_IQ2X, MAXM, LPR2_, CPL2_, 64, SCPL_>(a, max_active, h, hs, st);             \
     }
         MOE_GU(4096, 64, 1, 64, 2, 8)

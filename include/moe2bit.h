@@ -84,7 +84,8 @@ typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GENERIC = 1, MOE_PATH_GEMV = 2, MOE_P
  *     in the PREPARED layout written by moe_prepare_weights (same byte count
  *     as the canonical blocks).  gate_up_fmt is iq2x or q4k; down_fmt is q2k
  *     or q4k.
- *   codebook: device, 256 x 8 uint8 magnitudes in {1, 2, 3} (iq2x only).
+ *   codebook: device, 256 x 8 uint8 magnitudes in {1, 2, 3}, 8-byte aligned
+ *     (iq2x only).
  *   shared_inter (Is): 0 = no shared expert; else shared_gate, shared_up
  *     [Is][H] and shared_down [H][Is], bf16 row-major.
  *   path: kernel family for moe_expert_ffn (MOE_PATH_AUTO normally).
