@@ -64,11 +64,29 @@ __device__ __forceinline__ uint32_t codebook_row_fp4(const uint8_t *cb, int e) {
 // Sign bits of an 8-weight sub-group spread onto fp4 sign positions (bit 4i+3);
 // the eighth sign is the parity of the seven stored ones.
 __device__ __forceinline__ uint32_t sign_spread(uint32_t s7) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 7; ++i) w |= ((s7 >> i) & 1u) << (4 * i + 3);
-    w |= (uint32_t)(__builtin_popcount(s7) & 1) << 31;
-    return w;
+    uint32_t x = s7 | ((uint32_t)(__builtin_popcount(s7) & 1) << 7);    // eight sign bits
+    x = (x | (x << 12)) & 0x000F000Fu;                                   // bit i -> 4i in three doubling steps
+    x = (x | (x << 6)) & 0x03030303u;
+    x = (x | (x << 3)) & 0x11111111u;
+    return x << 3;
+}
+
+// A codebook row as two little-endian words of magnitude bytes (1, 2, 3) ->
+// eight fp4 codes (2, 4, 5), nibble i = weight i.  Per byte 2m - [m == 3],
+// then the bytes are packed into nibbles.
+__device__ __forceinline__ uint32_t cbrow_fp4(uint32_t x, uint32_t y) {
+    const uint32_t lo = (x << 1) - ((x >> 1) & x & 0x01010101u);
+    const uint32_t hi = (y << 1) - ((y >> 1) & y & 0x01010101u);
+    const uint32_t l2 = (lo | (lo >> 4)) & 0x00FF00FFu, h2 = (hi | (hi >> 4)) & 0x00FF00FFu;
+    return ((l2 | (l2 >> 8)) & 0xFFFFu) | (((h2 | (h2 >> 8)) & 0xFFFFu) << 16);
+}
+
+// 2s + 1 for the 4-bit group scale s of an iq2x group held as the two words
+// of its four prepared fields: scale bit i is bit 15 of field i.
+__device__ __forceinline__ uint32_t iq2x_gscale(uint32_t lo, uint32_t hi) {
+    uint32_t u = ((lo >> 14) & 0x00020002u) | 1u;          // s0 -> bit 1, s1 -> bit 17
+    u |= (hi >> 12) & 0x00080008u;                         // s2 -> bit 3, s3 -> bit 19
+    return (u | (u >> 15)) & 0x1Fu;
 }
 
 // Two fp4 codes (byte `sel` of v) -> bf16 / f16 / f32 pairs, unscaled.

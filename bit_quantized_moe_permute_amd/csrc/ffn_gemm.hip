@@ -285,8 +285,7 @@ __device__ __forceinline__ void gu_block(const GuW &w, const uint4 *tile, const 
         for (int gi = 0; gi < 4; ++gi) {
             const uint4 qq = w.q[f][gi >> 1];
             const uint32_t lo = (gi & 1) ? qq.z : qq.x, hi = (gi & 1) ? qq.w : qq.y;
-            const uint32_t s = ((lo >> 15) & 1u) | ((lo >> 30) & 2u) | ((hi >> 13) & 4u) | ((hi >> 28) & 8u);
-            mul[f][gi] = f16pair((2u * s + 1u) & keep);
+            mul[f][gi] = f16pair(iq2x_gscale(lo, hi) & keep);
         }
     }
     // phase 1: all 32 codebook/sign lookups of the block at once (one LDS round trip)
@@ -346,12 +345,14 @@ __device__ __forceinline__ void gu_loop(const FfnArgs &a, int e, int row, int hh
         const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
         x_fetch(src, k1 * KB, xs);
         gu_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w1);
+        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         gu_block<two>(w0, tiles[0], cb4, sgn, n, hh, dprev, acc);
         x_store(xs, tiles[1]);
         __syncthreads();
         if (kb + 1 >= nkb) break;
         x_fetch(src, k2 * KB, xs);
         gu_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w0);
+        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         gu_block<two>(w1, tiles[1], cb4, sgn, n, hh, dprev, acc);
         x_store(xs, tiles[0]);
         __syncthreads();
@@ -470,12 +471,14 @@ __device__ __forceinline__ void q4_loop(const uint8_t *W, int64_t NB, int64_t bl
         const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
         x_fetch(src, k1 * KB, xs);
         q4_load(W, NB, bl0 + k1, hh, w1);
+        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         q4_block<two>(w0, tiles[0], hs[0], n, hh, dprev, mprev, acc, accm);
         x_store_sums32(xs, tiles[1], hs[1]);
         __syncthreads();
         if (kb + 1 >= nkb) break;
         x_fetch(src, k2 * KB, xs);
         q4_load(W, NB, bl0 + k2, hh, w0);
+        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         q4_block<two>(w1, tiles[1], hs[1], n, hh, dprev, mprev, acc, accm);
         x_store_sums32(xs, tiles[0], hs[0]);
         __syncthreads();
@@ -530,8 +533,10 @@ __device__ __forceinline__ void sg_loop(const FfnArgs &a, int row, int hh, int n
         const bool block_start = (st & 3) == 0;
         if (block_start) x_fetch(src, min(kb + 1, nkb - 1) * KB, xs);
         sg_stage_load(a, row, hh, st + 1, b1);
+        __builtin_amdgcn_sched_barrier(0);
         sg_stage<two>(b0, tiles[kb & 1], st, n, hh, acc);
         sg_stage_load(a, row, hh, min(st + 2, nst - 1), b0);
+        __builtin_amdgcn_sched_barrier(0);
         sg_stage<two>(b1, tiles[kb & 1], st + 1, n, hh, acc);
         if (!block_start) {                              // end of block kb: publish tile kb + 1
             x_store(xs, tiles[(kb + 1) & 1]);
@@ -750,6 +755,7 @@ __device__ __forceinline__ void dn_loop(const FfnArgs &a, int e, int row, int hh
         __syncthreads();
         x_fetch(src, k1 * KB, xs);
         dn_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w1);
+        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         dn_block<two>(w0, tiles[0], hsum, n, hh, dprev, mprev, acc, accm);
         x_store(xs, tiles[1]);
         __syncthreads();
@@ -758,6 +764,7 @@ __device__ __forceinline__ void dn_loop(const FfnArgs &a, int e, int row, int hh
         __syncthreads();
         x_fetch(src, k2 * KB, xs);
         dn_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w0);
+        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         dn_block<two>(w1, tiles[1], hsum, n, hh, dprev, mprev, acc, accm);
         x_store(xs, tiles[0]);
         __syncthreads();
@@ -804,12 +811,14 @@ __device__ __forceinline__ void sd_loop(const FfnArgs &a, int row, int hh, int n
         const int s1 = min(st + 1, nst - 1), s2 = min(st + 2, nst - 1);
         x_fetch_hilo(hi, lo, s1 * 128, xs);
         sd_stage_load(a, row, hh, s1, b1);
+        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         sd_stage<two>(b0, tiles[0], n, hh, acc);
         x_store(xs, tiles[1]);
         __syncthreads();
         if (st + 1 >= nst) break;
         x_fetch_hilo(hi, lo, s2 * 128, xs);
         sd_stage_load(a, row, hh, s2, b0);
+        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         sd_stage<two>(b1, tiles[1], n, hh, acc);
         x_store(xs, tiles[0]);
         __syncthreads();

@@ -326,44 +326,46 @@ template <int MAXM> __device__ __forceinline__ void all_tokens(const FfnArgs &a,
 // ---------------------------------------------------------------------------
 // iq2x gate/up on the matrix cores (T <= 4 tokens per expert).
 //
-// v_mfma_f32_16x16x32_fp8_fp8 with the weights as B (32 K x 16 rows) and the
-// activations as A.  Codebook magnitudes 1, 2, 3 and their signs are exact in
-// fp8 (e4m3), so an 8-weight sub-group is two LDS lookups (codebook row as
-// eight fp8 bytes, sign byte spread to the 0x80 bits) and an OR: no
-// conversion.  Activations are split into two e4m3 pieces per 32-value group,
-// hi = e4m3(x') and lo = e4m3(x' - hi) with x' = x * 2^s, 2^s the power of two
-// that brings the group's max|x| into [128, 256); for |x'| >= 2^-2 the two
-// pieces hold all eight significant bits of the bf16 value, and the group's
-// sums pick up 2^-s with the weight scales.
+// gfx950's v_mfma_f32_16x16x128_f8f6f4 with mixed operand formats: B = the
+// weights in fp4 (E2M1), A = the activations in fp8 (E4M3).  Codebook
+// magnitudes 1, 2, 3 and their signs are exact E2M1 codes, so an 8-weight
+// sub-group is two 4-byte LDS lookups and an OR (codebook row as eight fp4
+// codes, 7-bit sign index spread onto the code sign bits with the parity
+// sign), fed to the instruction with no conversion.  Activations are split
+// into two e4m3 pieces per 32-value group, hi = e4m3(x') and lo =
+// e4m3(x' - hi) with x' = x * 2^s, 2^s the power of two that brings the
+// group's max|x| into [128, 256); for |x'| >= 2^-2 the two pieces hold all
+// eight significant bits of the bf16 value, and the group's sums pick up 2^-s
+// with the weight scales.
 //
+// Operand layouts of the instruction (one 128-wide K step, lane = 16 g + i):
+//   B (fp4): lane holds column i, K 32g .. 32g+31 (nibble j of register p = K 32g + 8p + j);
+//   A (fp8): lane holds row i, K 16g .. 16g+15 (bytes 0..15) and 64 + 16g .. 64 + 16g + 15 (bytes 16..31);
+//   D:       lane holds column i, rows 4g .. 4g+3.
 // Lane (n, q) (n = lane % 16, q = lane / 16) decodes row n; in every
-// 256-weight block quarter q takes 16-byte chunk q (groups q and q + 4), so a
-// lane owns whole groups and their 4-bit scales.  The pieces of token t sit in
-// A rows 4q + 2t + p (p: 0 hi, 1 lo, t < 2 per product), non-zero only in the K
-// quarter q: quarter q's products land in D rows 4q .. 4q+3, which the lanes
-// of quarter q hold.  A group is 4 K-steps into a fresh accumulator, then
-// added to the lane's running sums times (2s+1) * d * 2^-s(x).
+// 256-weight block it takes 16-byte chunk q (groups q and q + 4), and K step
+// h (h = 0, 1: block columns 128h .. 128h+127) pairs its group q + 4h with
+// B lane group q.  The pieces of token t sit in A row 4q' + 2t + p (p: 0 hi,
+// 1 lo, t < 2 per product), non-zero only for K in group q' of the step, so
+// group q' of every row lands in D rows 4q' .. 4q'+3 -- held by the lanes
+// that own that group's 4-bit scale.  Each step is a fresh product, added to
+// the lane's running sums times (2s+1) * d * 2^-s(x); the A operands depend
+// on the tokens only, so they are built once and serve every row.
 // A workgroup of H/512 waves takes one expert and MF_RB*16 rows, wave w the
 // K slice [512w, 512w+512); the slices and quarters are summed in LDS.
 // ---------------------------------------------------------------------------
 constexpr int MF_KW = 512;
-constexpr int MF_RB = 4;
+constexpr int MF_RB = 2;
 constexpr int MF_MAXH = 4096;
 
-// index: sign byte of a prepared field (7 signs, bit 7 belongs to the group scale)
-__device__ __forceinline__ uint64_t sign_fp8(int b) {
-    const uint32_t s7 = (uint32_t)b & 0x7Fu;
-    const uint32_t bits = s7 | ((__builtin_popcount(s7) & 1u) << 7);
-    uint64_t r = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r |= (uint64_t)((bits >> j) & 1u) << (8 * j + 7);
-    return r;
-}
-
 typedef __attribute__((ext_vector_type(4))) float mf_acc_t;
+typedef __attribute__((ext_vector_type(8))) int mf_ab_t;
 
-__device__ __forceinline__ mf_acc_t mfma_fp8(uint64_t a, uint64_t b, mf_acc_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)a, (long)b, c, 0, 0, 0);
+// D = A (fp8 e4m3, 32 bytes per lane) x B (fp4 e2m1, 16 bytes per lane), unscaled
+__device__ __forceinline__ mf_acc_t mfma_f8f4(const mf_ab_t &a, uint4 b) {
+    const mf_ab_t bb = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    const mf_acc_t zero = {};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, zero, 0, 4, 0, 0, 0, 0);
 }
 
 // active, offsets, perm: the routing arrays, read-only here; with uniform
@@ -373,9 +375,9 @@ template <int MAXM>
 __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32_t *__restrict__ active,
                                                    const int32_t *__restrict__ offsets,
                                                    const int32_t *__restrict__ perm, int ai, int row0,
-                                                   _Float16 *__restrict__ h, uint64_t *cb8, uint64_t *sg8,
+                                                   _Float16 *__restrict__ h, uint32_t *cb4, uint32_t *sgn,
                                                    uint8_t (*xq)[2][MF_MAXH], float (*xsc)[MF_MAXH / 32], float *red) {
-    constexpr int NP = (MAXM + 1) / 2;                       // products per K-step (two tokens each)
+    constexpr int NP = (MAXM + 1) / 2;                       // products per K step (two tokens each)
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
     const int n = lane & 15, qd = lane >> 4;
     const int H = a.H, I = a.I;
@@ -398,16 +400,8 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = tid + i * (int)blockDim.x;
-        if (row < 256) {
-            uint64_t r = 0;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t mag = ((j < 4 ? cbrow[i].x : cbrow[i].y) >> (8 * (j & 3))) & 0xFFu;   // 1, 2 or 3
-                r |= (uint64_t)(mag == 1 ? 0x38u : (mag == 2 ? 0x40u : 0x44u)) << (8 * j);
-            }
-            cb8[row] = r;
-            sg8[row] = sign_fp8(row);
-        }
+        if (row < 256) cb4[row] = cbrow_fp4(cbrow[i].x, cbrow[i].y);
+        if (row < 128) sgn[row] = sign_spread(row);
     }
     // --- all weights of this wave: units u = (row block u / 2, K block u % 2)
     const int64_t nb_row = H / MOE_QK, nb_mat = (int64_t)I * nb_row, NB = nb_mat * a.E;
@@ -452,35 +446,31 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
         *reinterpret_cast<uint2 *>(&xq[m][1][8 * tid]) = make_uint2(lo2[0], lo2[1]);
     }
     if (ai >= n_active) return;                               // whole workgroup: fewer experts than launched
-    // --- the expert's tokens (slot t*k + j in the permutation)
-    Tokens<MAXM> tk;
-    {
-        const int o0 = offsets[e];
-        tk.n = min(offsets[e + 1] - o0, MAXM);
-#pragma unroll
-        for (int m = 0; m < MAXM; ++m) {
-            const int sl = perm[o0 + (m < tk.n ? m : 0)];
-            tk.slot[m] = sl;
-            tk.tok[m] = min(sl / a.k, MAXM - 1);
-        }
-    }
+    // --- every token of the call is multiplied (the products hold MAXM
+    // tokens whichever are routed here); the expert's own tokens are picked
+    // in the epilogue, so no routing load waits behind the weight stream.
+    const int nt = min(a.T, MAXM);
     __syncthreads();
-    // --- A operand of this lane: A row n = 4 qa + 2 t + p holds slot (2 pr + t), piece p, in K quarter qa
-    const bool arow = (n >> 2) == qd;
-    const int at0 = (n >> 1) & 1, ap = n & 1;
-    int axt[NP];
-    bool aval[NP];
+    // --- A operands [K block][K step][product]: A row n = 4 qa + 2 t + p holds
+    // token (2 pr + t), piece p, for the K values of group qa of the step; this
+    // lane holds 16 of them when lane group qd covers half of that group.
+    const int qa = n >> 2, at0 = (n >> 1) & 1, ap = n & 1;
+    const bool arow = (qd >> 1) == (qa & 1);
+    mf_ab_t A[2][2][NP];
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr) {
-        const int sl = 2 * pr + at0;
-        aval[pr] = arow && sl < tk.n;
-        int tt = 0;
+        const int tt = min(2 * pr + at0, MAXM - 1);
+        const bool val = arow && 2 * pr + at0 < nt;
 #pragma unroll
-        for (int m = 0; m < MAXM; ++m)
-            if (m == sl) tt = tk.tok[m];
-        axt[pr] = tt;
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs) {
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (val) v = *reinterpret_cast<const uint4 *>(&xq[tt][ap][k0w + 256 * b + 128 * hs + 32 * qa + 16 * (qd & 1)]);
+                const uint4 lo = qa < 2 ? v : make_uint4(0u, 0u, 0u, 0u), hi = qa < 2 ? make_uint4(0u, 0u, 0u, 0u) : v;
+                A[b][hs][pr] = mf_ab_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
     }
-    const mf_acc_t zero = {};
     float tot[2][MAXM];
 #pragma unroll
     for (int f = 0; f < 2; ++f)
@@ -491,34 +481,29 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
         const int b = u & 1;
         const float dsc[2] = {f16_bits_to_f32(wd[u] & 0xFFFFu), f16_bits_to_f32(wd[u] >> 16)};
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {                              // group qd + 4 gi of the block
-            const int kg = k0w + 256 * b + 32 * (qd + 4 * gi);       // first column of the group
+        for (int hs = 0; hs < 2; ++hs) {                              // K step hs: this lane's group qd + 4 hs
+            const int kg = k0w + 256 * b + 32 * (qd + 4 * hs);       // first column of the group
             mf_acc_t acc[2][NP];
-#pragma unroll
-            for (int ps = 0; ps < 4; ++ps) {
-                uint64_t A[NP];
-#pragma unroll
-                for (int pr = 0; pr < NP; ++pr)
-                    A[pr] = aval[pr] ? *reinterpret_cast<const uint64_t *>(&xq[axt[pr]][ap][kg + 8 * ps]) : 0ull;
-#pragma unroll
-                for (int f = 0; f < 2; ++f) {
-                    const uint4 c = wq[u][f];
-                    const uint32_t dw = gi ? ((ps >> 1) ? c.w : c.z) : ((ps >> 1) ? c.y : c.x);
-                    const uint32_t fld = (ps & 1) ? (dw >> 16) : (dw & 0xFFFFu);
-                    const uint64_t wb = cb8[fld & 0xFFu] | sg8[fld >> 8];
-#pragma unroll
-                    for (int pr = 0; pr < NP; ++pr) acc[f][pr] = mfma_fp8(A[pr], wb, ps == 0 ? zero : acc[f][pr]);
-                }
-            }
-            float xs[MAXM];
-#pragma unroll
-            for (int m = 0; m < MAXM; ++m) xs[m] = xsc[tk.tok[m]][kg >> 5];
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
                 const uint4 c = wq[u][f];
-                const uint32_t lo = gi ? c.z : c.x, hi = gi ? c.w : c.y;
-                const uint32_t sg = ((lo >> 15) & 1u) | ((lo >> 30) & 2u) | ((hi >> 13) & 4u) | ((hi >> 28) & 8u);
-                const float S = dsc[f] * (float)(2u * sg + 1u);
+                const uint32_t lo = hs ? c.z : c.x, hi = hs ? c.w : c.y;
+                uint4 bw;
+                bw.x = cb4[lo & 0xFFu] | sgn[(lo >> 8) & 0x7Fu];
+                bw.y = cb4[(lo >> 16) & 0xFFu] | sgn[(lo >> 24) & 0x7Fu];
+                bw.z = cb4[hi & 0xFFu] | sgn[(hi >> 8) & 0x7Fu];
+                bw.w = cb4[(hi >> 16) & 0xFFu] | sgn[(hi >> 24) & 0x7Fu];
+#pragma unroll
+                for (int pr = 0; pr < NP; ++pr) acc[f][pr] = mfma_f8f4(A[b][hs][pr], bw);
+            }
+            float xs[MAXM];
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) xs[m] = m < nt ? xsc[m][kg >> 5] : 0.f;
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                const uint4 c = wq[u][f];
+                const uint32_t lo = hs ? c.z : c.x, hi = hs ? c.w : c.y;
+                const float S = dsc[f] * (float)iq2x_gscale(lo, hi);
 #pragma unroll
                 for (int m = 0; m < MAXM; ++m) {
                     const mf_acc_t &d = acc[f][m >> 1];
@@ -542,16 +527,19 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
         }
     }
     __syncthreads();
+    // --- the expert's tokens: entry j of its run in the permutation is slot t*k + j'
+    const int o0 = offsets[e], ne = min(offsets[e + 1] - o0, MAXM);
     for (int i = tid; i < MF_RB * MAXM * 16; i += blockDim.x) {
-        const int nn = i & 15, m = (i >> 4) % MAXM, rb = (i >> 4) / MAXM;
+        const int nn = i & 15, j = (i >> 4) % MAXM, rb = (i >> 4) / MAXM;
         const int r = row0 + 16 * rb + nn;
-        if (m >= tk.n || r >= I) continue;
+        if (j >= ne || r >= I) continue;
+        const int sl = perm[o0 + j], m = min(sl / a.k, MAXM - 1);
         float g = 0.f, u = 0.f;
         for (int w = 0; w < nw; ++w) {
             g += red[(((w * MF_RB + rb) * 2 + 0) * MAXM + m) * 16 + nn];
             u += red[(((w * MF_RB + rb) * 2 + 1) * MAXM + m) * 16 + nn];
         }
-        h[(int64_t)tk.slot[m] * I + r] = (_Float16)silu_mul(g, u);
+        h[(int64_t)sl * I + r] = (_Float16)silu_mul(g, u);
     }
 }
 
@@ -562,14 +550,14 @@ __global__ __launch_bounds__(512) void k_gemv_gateup_mfma(FfnArgs a, const int32
                                                            const int32_t *__restrict__ perm, int wgs_per_expert,
                                                            int n_routed_wgs, _Float16 *__restrict__ h,
                                                            float *__restrict__ hs) {
-    __shared__ uint64_t cb8[256], sg8[256];
+    __shared__ uint32_t cb4[256], sgn[128];
     __shared__ __attribute__((aligned(16))) uint8_t xq[MAXM][2][MF_MAXH];
     __shared__ float xsc[MAXM][MF_MAXH / 32];
     __shared__ float red[(MF_MAXH / MF_KW) * MF_RB * 2 * MAXM * 16];
     const int bid = blockIdx.x;
     if (bid < n_routed_wgs) {
         const int ai = bid / wgs_per_expert;
-        routed_gateup_mfma<MAXM>(a, active, offsets, perm, ai, (bid % wgs_per_expert) * (16 * MF_RB), h, cb8, sg8,
+        routed_gateup_mfma<MAXM>(a, active, offsets, perm, ai, (bid % wgs_per_expert) * (16 * MF_RB), h, cb4, sgn,
                                  xq, xsc, red);
     } else {
         Tokens<MAXM> tk;
