@@ -368,13 +368,13 @@ __device__ __forceinline__ mf_acc_t mfma_f8f4(const mf_ab_t &a, uint4 b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, zero, 0, 4, 0, 0, 0, 0);
 }
 
-// active, offsets, perm: the routing arrays, read-only here; with uniform
-// indices they are read through the scalar cache, whose wait counter is
-// separate from the weight loads in flight.
+// active: the active-expert list, read-only here; with uniform indices it is
+// read through the scalar cache, whose wait counter is separate from the
+// weight loads in flight.  The expert's slots come from topk_idx (T*k <= 64
+// entries, one per lane), requested before the weights and used at the end.
 template <int MAXM>
-__device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32_t *__restrict__ active,
-                                                   const int32_t *__restrict__ offsets,
-                                                   const int32_t *__restrict__ perm, int ai, int row0,
+__device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32_t *__restrict__ active, int ai,
+                                                   int row0,
                                                    _Float16 *__restrict__ h, uint32_t *cb4, uint32_t *sgn,
                                                    uint8_t (*xq)[2][MF_MAXH], float (*xsc)[MF_MAXH / 32], float *red) {
     constexpr int NP = (MAXM + 1) / 2;                       // products per K step (two tokens each)
@@ -382,27 +382,24 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
     const int n = lane & 15, qd = lane >> 4;
     const int H = a.H, I = a.I;
     const int k0w = wv * MF_KW;
-    // --- expert id (scalar), codebook rows and activations first: their loads
-    // complete before the weights' in issue order
+    // --- expert id (scalar); slot experts, codebook rows and activations are
+    // requested by every wave (unconditional loads, clamped indices) before
+    // any wave requests weights, and the tables and activation pieces are
+    // built while the weights stream in.
     const int n_active = active[0];
     const int e = min(max(active[1 + ai], 0), a.E - 1);      // in range even for an idle workgroup
+    const int n_slots = a.T * a.k;
+    const int sel_raw = a.topk_idx[min(lane, n_slots - 1)];
     uint2 cbrow[4];                                          // rows tid + i * blockDim (blockDim >= 64)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = tid + i * (int)blockDim.x;
-        cbrow[i] = r < 256 ? reinterpret_cast<const uint2 *>(a.codebook)[r] : make_uint2(0u, 0u);
-    }
+    for (int i = 0; i < 4; ++i) cbrow[i] = reinterpret_cast<const uint2 *>(a.codebook)[min(tid + i * (int)blockDim.x, 255)];
     uint4 xv[MAXM];
 #pragma unroll
     for (int m = 0; m < MAXM; ++m)
-        if (m < a.T)
-            xv[m] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + (int64_t)m * H + 8 * tid);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = tid + i * (int)blockDim.x;
-        if (row < 256) cb4[row] = cbrow_fp4(cbrow[i].x, cbrow[i].y);
-        if (row < 128) sgn[row] = sign_spread(row);
-    }
+        xv[m] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + (int64_t)min(m, a.T - 1) * H + 8 * tid);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     // --- all weights of this wave: units u = (row block u / 2, K block u % 2)
     const int64_t nb_row = H / MOE_QK, nb_mat = (int64_t)I * nb_row, NB = nb_mat * a.E;
     uint4 wq[2 * MF_RB][2];                                  // [unit][matrix]: chunk qd of the block
@@ -416,11 +413,22 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
         wd[u] = (uint32_t)reinterpret_cast<const uint16_t *>(a.gate + NB * 64)[bl] |
                 ((uint32_t)reinterpret_cast<const uint16_t *>(a.up + NB * 64)[bl] << 16);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    const int sel = lane < n_slots ? sel_raw : -1;           // slot `lane`'s expert
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = tid + i * (int)blockDim.x;
+        if (row < 256) cb4[row] = cbrow_fp4(cbrow[i].x, cbrow[i].y);
+        if (row < 256) sgn[row] = sign_spread(row & 0x7F);   // indexed by a field's whole high byte
+    }
     // --- activation pieces of every token of the call: thread tid converts
     // x[t][8 tid .. 8 tid + 7]; the four threads of a 32-value group share 2^s
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
-        if (m >= a.T) break;
+        if (m >= a.T) {                                      // no token: zero scale, pieces never read
+            if ((tid & 3) == 0) xsc[m][tid >> 2] = 0.f;
+            continue;
+        }
         const uint32_t w4[4] = {xv[m].x, xv[m].y, xv[m].z, xv[m].w};
         float mx = 0.f;
 #pragma unroll
@@ -480,25 +488,30 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
     for (int u = 0; u < 2 * MF_RB; ++u) {
         const int b = u & 1;
         const float dsc[2] = {f16_bits_to_f32(wd[u] & 0xFFFFu), f16_bits_to_f32(wd[u] >> 16)};
+        // all four products of the unit first (K steps hs = 0, 1: this lane's
+        // groups qd and qd + 4), then their scales, so that no scale waits
+        // on the product just issued
+        mf_acc_t acc[2][2][NP];
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {                              // K step hs: this lane's group qd + 4 hs
-            const int kg = k0w + 256 * b + 32 * (qd + 4 * hs);       // first column of the group
-            mf_acc_t acc[2][NP];
+        for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
                 const uint4 c = wq[u][f];
                 const uint32_t lo = hs ? c.z : c.x, hi = hs ? c.w : c.y;
                 uint4 bw;
-                bw.x = cb4[lo & 0xFFu] | sgn[(lo >> 8) & 0x7Fu];
-                bw.y = cb4[(lo >> 16) & 0xFFu] | sgn[(lo >> 24) & 0x7Fu];
-                bw.z = cb4[hi & 0xFFu] | sgn[(hi >> 8) & 0x7Fu];
-                bw.w = cb4[(hi >> 16) & 0xFFu] | sgn[(hi >> 24) & 0x7Fu];
+                bw.x = cb4[lo & 0xFFu] | sgn[(lo >> 8) & 0xFFu];
+                bw.y = cb4[(lo >> 16) & 0xFFu] | sgn[lo >> 24];
+                bw.z = cb4[hi & 0xFFu] | sgn[(hi >> 8) & 0xFFu];
+                bw.w = cb4[(hi >> 16) & 0xFFu] | sgn[hi >> 24];
 #pragma unroll
-                for (int pr = 0; pr < NP; ++pr) acc[f][pr] = mfma_f8f4(A[b][hs][pr], bw);
+                for (int pr = 0; pr < NP; ++pr) acc[hs][f][pr] = mfma_f8f4(A[b][hs][pr], bw);
             }
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            const int g = (k0w + 256 * b) / 32 + qd + 4 * hs;       // this lane's group
             float xs[MAXM];
 #pragma unroll
-            for (int m = 0; m < MAXM; ++m) xs[m] = m < nt ? xsc[m][kg >> 5] : 0.f;
+            for (int m = 0; m < MAXM; ++m) xs[m] = xsc[m][g];          // zero for tokens past T
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
                 const uint4 c = wq[u][f];
@@ -506,7 +519,7 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
                 const float S = dsc[f] * (float)iq2x_gscale(lo, hi);
 #pragma unroll
                 for (int m = 0; m < MAXM; ++m) {
-                    const mf_acc_t &d = acc[f][m >> 1];
+                    const mf_acc_t &d = acc[hs][f][m >> 1];
                     const float v = (m & 1) ? d[2] + d[3] : d[0] + d[1];
                     tot[f][m] = __fmaf_rn(S * xs[m], v, tot[f][m]);
                 }
@@ -527,13 +540,15 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
         }
     }
     __syncthreads();
-    // --- the expert's tokens: entry j of its run in the permutation is slot t*k + j'
-    const int o0 = offsets[e], ne = min(offsets[e + 1] - o0, MAXM);
+    // --- token m's slot for this expert: m*k + j where topk_idx[m][j] == e (at most one j)
+    const uint64_t hit = __ballot(sel == e);
+    const uint64_t kmask = a.k >= 64 ? ~0ull : (1ull << a.k) - 1ull;
     for (int i = tid; i < MF_RB * MAXM * 16; i += blockDim.x) {
-        const int nn = i & 15, j = (i >> 4) % MAXM, rb = (i >> 4) / MAXM;
+        const int nn = i & 15, m = (i >> 4) % MAXM, rb = (i >> 4) / MAXM;
         const int r = row0 + 16 * rb + nn;
-        if (j >= ne || r >= I) continue;
-        const int sl = perm[o0 + j], m = min(sl / a.k, MAXM - 1);
+        const uint64_t hm = m < a.T ? (hit >> (m * a.k)) & kmask : 0ull;
+        if (hm == 0ull || r >= I) continue;
+        const int sl = m * a.k + (__builtin_ffsll((long long)hm) - 1);
         float g = 0.f, u = 0.f;
         for (int w = 0; w < nw; ++w) {
             g += red[(((w * MF_RB + rb) * 2 + 0) * MAXM + m) * 16 + nn];
@@ -546,19 +561,16 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
 // Routed iq2x rows on the matrix cores, shared bf16 rows as in k_gemv_gateup.
 template <int SLPR, int SCPL, int MAXM>
 __global__ __launch_bounds__(512) void k_gemv_gateup_mfma(FfnArgs a, const int32_t *__restrict__ active,
-                                                           const int32_t *__restrict__ offsets,
-                                                           const int32_t *__restrict__ perm, int wgs_per_expert,
-                                                           int n_routed_wgs, _Float16 *__restrict__ h,
-                                                           float *__restrict__ hs) {
-    __shared__ uint32_t cb4[256], sgn[128];
+                                                           int wgs_per_expert, int n_routed_wgs,
+                                                           _Float16 *__restrict__ h, float *__restrict__ hs) {
+    __shared__ uint32_t cb4[256], sgn[256];
     __shared__ __attribute__((aligned(16))) uint8_t xq[MAXM][2][MF_MAXH];
     __shared__ float xsc[MAXM][MF_MAXH / 32];
     __shared__ float red[(MF_MAXH / MF_KW) * MF_RB * 2 * MAXM * 16];
     const int bid = blockIdx.x;
     if (bid < n_routed_wgs) {
         const int ai = bid / wgs_per_expert;
-        routed_gateup_mfma<MAXM>(a, active, offsets, perm, ai, (bid % wgs_per_expert) * (16 * MF_RB), h, cb4, sgn,
-                                 xq, xsc, red);
+        routed_gateup_mfma<MAXM>(a, active, ai, (bid % wgs_per_expert) * (16 * MF_RB), h, cb4, sgn, xq, xsc, red);
     } else {
         Tokens<MAXM> tk;
         all_tokens<MAXM>(a, tk);
@@ -908,12 +920,13 @@ hipError_t run_gateup_mfma(const FfnArgs &a, int max_active, _Float16 *h, float 
         ns = (a.Is + srows - 1) / srows;
     }
     hipLaunchKernelGGL((k_gemv_gateup_mfma<SLPR, SCPL, MAXM>), dim3(nr + ns), dim3(threads), 0, st, a, a.active,
-                       a.offsets, a.perm, wpe, nr, h, hs);
+                       wpe, nr, h, hs);
     return hipGetLastError();
 }
 
 bool gateup_mfma_ok(const FfnArgs &a) {
-    return a.fmt_gu == FMT_IQ2X && a.H % MF_KW == 0 && a.H >= MF_KW && a.H <= MF_MAXH && a.I % (16 * MF_RB) == 0;
+    return a.fmt_gu == FMT_IQ2X && a.H % MF_KW == 0 && a.H >= MF_KW && a.H <= MF_MAXH && a.I % (16 * MF_RB) == 0 &&
+           a.T * a.k <= 64;
 }
 
 template <int FD, int MAXM, int LPR, int CPL, int SLPR, int SCPL>
