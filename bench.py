@@ -60,7 +60,7 @@ def parse():
 # WRITE_SIZE counters on that kernel, each scaled by the same counter's reading
 # for a 1 GiB device-to-device copy in the same process.  Valid only for the
 # kernel source it was measured on (sha256 of csrc/ffn_gemv.hip).
-GATEUP_TRAFFIC = {"src_sha256": "2057aa67f4221e588636c437cda15d3c16dbd2c6b4b1b9ec9a5ca5de89ce8a30", "bytes": 68916187}
+GATEUP_TRAFFIC = {"src_sha256": "9c30b3271f90747f36a0393b5dde9a6e94c5f92274c100c18d5d3ecc6a05ab0e", "bytes": 68459994}
 
 
 def gemv_source_sha():
@@ -257,7 +257,7 @@ def main():
     traffic = GATEUP_TRAFFIC["bytes"] if GATEUP_TRAFFIC["src_sha256"] == gemv_source_sha() else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_gemv_gateup_mfma (routed iq2x gate/up on fp8 MFMA + bf16 shared gate/up, fused SwiGLU)",
+                "kernel": "k_gemv_gateup_mfma (routed iq2x gate/up on fp8 x fp4 MFMA + bf16 shared gate/up, fused SwiGLU)",
                 "bytes_per_launch": nbytes["gate_up"], "avg_launch_us": round(gu_us, 3)}
     step_bw = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
 
