@@ -26,6 +26,11 @@ constexpr int WAVES = 4;
 // rows per wave for bf16 rows with CPL 16-byte chunks per lane
 template <int CPL> constexpr int shared_nr() { return CPL >= 4 ? 1 : 4 / CPL; }
 
+// Down projection for one token: twice the rows per wave (routed and shared),
+// so that the routed workgroups leave room for shared ones from the start.
+template <int MAXM> constexpr int nr_down() { return MAXM == 1 ? 8 : 4; }
+template <int CPL, int MAXM> constexpr int shared_nr_down() { return MAXM == 1 ? 2 * shared_nr<CPL>() : shared_nr<CPL>(); }
+
 template <int LPR> __device__ __forceinline__ float row_sum(float v) {
 #pragma unroll
     for (int o = LPR / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -869,7 +874,7 @@ __global__ __launch_bounds__(256) void k_gemv_down(FfnArgs a, int wgs_per_expert
     } else {
         Tokens<MAXM> tk;
         all_tokens<MAXM>(a, tk);
-        constexpr int SNR = shared_nr<SCPL>();
+        constexpr int SNR = shared_nr_down<SCPL, MAXM>();
         constexpr int ROWS = WAVES * SNR * (64 / SLPR);
         shared_down<SLPR, SCPL, MAXM, SNR>(a, tk, (bid - n_routed_wgs) * ROWS, hs);
     }
@@ -931,16 +936,17 @@ bool gateup_mfma_ok(const FfnArgs &a) {
 
 template <int FD, int MAXM, int LPR, int CPL, int SLPR, int SCPL>
 hipError_t run_down(const FfnArgs &a, int max_active, const _Float16 *h, const float *hs, hipStream_t st) {
-    const int rows = WAVES * NR * (64 / LPR);
+    constexpr int NRD = nr_down<MAXM>();
+    const int rows = WAVES * NRD * (64 / LPR);
     const int wpe = (a.H + rows - 1) / rows;
     const int nr = max_active * wpe;
     int ns = 0;
     if (a.Is > 0) {
-        const int srows = WAVES * shared_nr<SCPL>() * (64 / SLPR);
+        const int srows = WAVES * shared_nr_down<SCPL, MAXM>() * (64 / SLPR);
         ns = (a.H + srows - 1) / srows;
     }
-    hipLaunchKernelGGL((k_gemv_down<FD, LPR, CPL, SLPR, SCPL, MAXM, NR>), dim3(nr + ns), dim3(256), 0, st, a, wpe, nr,
-                       h, hs);
+    hipLaunchKernelGGL((k_gemv_down<FD, LPR, CPL, SLPR, SCPL, MAXM, NRD>), dim3(nr + ns), dim3(256), 0, st, a, wpe,
+                       nr, h, hs);
     return hipGetLastError();
 }
 
