@@ -4,7 +4,7 @@ Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
 may import this package.  The GPU library never does, and this package never
 imports the GPU library: the two share no code.  Every result here is computed
 in binary64 by the plain C in ``moe_oracle.c`` (formats, quantizers, router,
-permutation, SwiGLU experts, combine); this module only marshals numpy arrays.
+permutation, SwiGLU experts, combine, steering); this module only marshals numpy arrays.
 
 Sources: the routed experts are the only quantized tensors, up/gate in
 IQ2_XXS, down in Q2_K, shared experts and routing kept at full precision
@@ -13,9 +13,10 @@ IQ2_XXS, down in Q2_K, shared experts and routing kept at full precision
 philosophy).  The block layouts and arithmetic are this project's readings of
 those format names; see the header comment of moe_oracle.c.
 
-Parity status: formats, quantizers, routing, permutation, FFN and combine are
-each pinned by tests in tests/test_oracle_*.py (hand-worked blocks, closed
-forms, library routines on the special cases, brute force, invariants).
+Parity status: formats, quantizers, routing, permutation, FFN, combine and
+steering are each pinned by tests in tests/test_oracle_*.py (hand-worked
+blocks, closed forms, library routines on the special cases, brute force,
+invariants).
 """
 from __future__ import annotations
 
@@ -68,6 +69,7 @@ def lib():
         L.oracle_expert_ffn.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, vp]
         L.oracle_shared_ffn.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
         L.oracle_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+        L.oracle_steer.argtypes = [vp, vp, ctypes.c_double, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -200,9 +202,23 @@ def combine(slot_out, topk_w, shared_out=None):
     return y
 
 
-def layer(x, w_router, k, n_experts, inter, fmt_gu, Wg, Wu, fmt_d, Wd, codebook, bias=None, shared=None):
+def steer(y, v, F):
+    """y[t] - F * v * dot(v, y[t]) per token in binary64 (directional steering of the FFN output)."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    T, H = y.shape
+    v = np.ascontiguousarray(v, dtype=np.float64).reshape(-1)
+    if v.shape[0] != H:
+        raise ValueError("steering direction must have one entry per hidden unit")
+    out = np.empty_like(y)
+    lib().oracle_steer(_p(y), _p(v), float(F), T, H, _p(out))
+    return out
+
+
+def layer(x, w_router, k, n_experts, inter, fmt_gu, Wg, Wu, fmt_d, Wd, codebook, bias=None, shared=None,
+          steering=None):
     """Whole layer: route -> permute -> routed experts (+ shared) -> combine.
 
+    ``steering`` = (v, F) applies directional steering to the combined output.
     Returns a dict with every intermediate the GPU path exposes.
     """
     logits, idx, tw = route(x, w_router, k, bias)
@@ -210,5 +226,7 @@ def layer(x, w_router, k, n_experts, inter, fmt_gu, Wg, Wu, fmt_d, Wd, codebook,
     slot_out = expert_ffn(x, idx, fmt_gu, Wg, Wu, fmt_d, Wd, codebook, n_experts, inter)
     s = shared_ffn(x, *shared) if shared is not None else None
     y = combine(slot_out, tw, s)
+    if steering is not None:
+        y = steer(y, *steering)
     return dict(logits=logits, topk_idx=idx, topk_w=tw, offsets=offsets, perm=perm, active=active,
                 slot_out=slot_out, shared_out=s, y=y)

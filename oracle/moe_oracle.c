@@ -510,3 +510,20 @@ void oracle_combine(const double *slot_out, const double *topk_w, const double *
             y[(int64_t)t * H + c] = acc;
         }
 }
+
+/*
+ * Directional steering of the FFN output ("DwarfStar4 / ds4.c" user report on
+ * modu-print.com, the ds4-server option listing, the FFN steering option): with
+ * one direction v per layer and a strength F, every token's FFN output y loses
+ * F times its component along v, y' = y - F * v * dot(v, y).  v is taken as
+ * given (not normalised); dot(v, y) runs over c in increasing order, binary64.
+ * y and out may be the same array.
+ */
+void oracle_steer(const double *y, const double *v, double F, int T, int H, double *out) {
+    for (int t = 0; t < T; t++) {
+        const double *yt = y + (int64_t)t * H;
+        double d = 0.0;
+        for (int c = 0; c < H; c++) d += v[c] * yt[c];
+        for (int c = 0; c < H; c++) out[(int64_t)t * H + c] = yt[c] - F * v[c] * d;
+    }
+}

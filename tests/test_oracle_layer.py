@@ -189,6 +189,57 @@ def test_combine_is_weighted_sum():
     assert np.allclose(y2, 2 * (want - s), rtol=1e-14, atol=1e-13)
 
 
+# directional steering of the FFN output: y' = y - F v (v . y)
+
+def test_steer_zero_strength_and_basis_direction():
+    g = np.random.default_rng(11)
+    T, H = 4, 48
+    y = g.standard_normal((T, H))
+    v = g.standard_normal(H)
+    assert np.array_equal(oracle.steer(y, v, 0.0), y)
+    # along a basis vector the map scales that one column by (1 - F), exactly
+    for i, F in ((0, 1.0), (17, 0.5), (47, 2.0)):
+        e = np.zeros(H)
+        e[i] = 1.0
+        out = oracle.steer(y, e, F)
+        want = y.copy()
+        want[:, i] = (1.0 - F) * y[:, i]
+        assert np.array_equal(out, want)
+
+
+def test_steer_unit_direction_projects_and_reflects():
+    g = np.random.default_rng(12)
+    T, H = 6, 4096
+    y = g.standard_normal((T, H))
+    v = g.standard_normal(H)
+    v /= np.linalg.norm(v)
+    p = oracle.steer(y, v, 1.0)
+    # F = 1 removes the component along v: orthogonal to v, and a projection (idempotent)
+    assert np.abs(p @ v).max() <= 1e-12 * np.abs(y).sum(axis=1).max()
+    assert np.allclose(oracle.steer(p, v, 1.0), p, rtol=0, atol=1e-13)
+    assert np.allclose(y - p, np.outer(y @ v, v), rtol=0, atol=1e-12)
+    # F = 2 is the Householder reflection: norm-preserving and its own inverse
+    r = oracle.steer(y, v, 2.0)
+    assert np.allclose(np.linalg.norm(r, axis=1), np.linalg.norm(y, axis=1), rtol=1e-13)
+    assert np.allclose(oracle.steer(r, v, 2.0), y, rtol=0, atol=1e-12)
+    assert np.allclose(r @ v, -(y @ v), rtol=1e-12, atol=1e-12)
+
+
+def test_steer_is_per_token_linear_and_unnormalised():
+    g = np.random.default_rng(13)
+    T, H = 5, 96
+    y1, y2 = g.standard_normal((T, H)), g.standard_normal((T, H))
+    v = g.standard_normal(H)
+    F = 0.75
+    out = oracle.steer(y1, v, F)
+    # rows are independent: reversing the tokens reverses the output rows bit for bit
+    assert np.array_equal(oracle.steer(y1[::-1], v, F), out[::-1])
+    # linear in y
+    assert np.allclose(oracle.steer(2 * y1 - 3 * y2, v, F), 2 * out - 3 * oracle.steer(y2, v, F), rtol=0, atol=1e-12)
+    # v is used as given: scaling it by c scales the strength by c^2
+    assert np.allclose(oracle.steer(y1, 3.0 * v, F), oracle.steer(y1, v, 9.0 * F), rtol=0, atol=1e-11)
+
+
 def test_layer_is_per_token(small):
     """Splitting the tokens into chunks, reordering them or duplicating one leaves
     every token's output bit-identical (the layer has no cross-token arithmetic)."""
