@@ -216,6 +216,17 @@ def main():
               "us_per_step": round(vwall * 1e6 / vK, 2)}
     log(f"verify: {vK} steps of 3 tokens -> {3 * vK / vwall:.0f} tokens/s, {vwall * 1e6 / vK:.1f} us/step")
 
+    # directional steering of the FFN output (y -= F v (v . y)), fused into the combine
+    steer_v = synth.steer_direction(H)
+    for Lc in layers:
+        Lc.set_steering(steer_v, 1.0)
+    swall, _ = graph_steps(step, K, W)
+    for Lc in layers:
+        Lc.set_steering(None)
+    steer = {"tokens_per_s": round(K / swall, 1), "ms_per_step": round(swall * 1e3 / K, 5),
+             "combine": combine_bench(k, H, (1, 3, 2048), args.kernel_reps or 200)}
+    log(f"decode with steering: {K / swall:.0f} tokens/s; combine kernels {steer['combine']}")
+
     # dominant kernel: gate/up (+SwiGLU) GEMV, routed and shared rows in one launch
     reps = args.kernel_reps or K
     log(f"timing the gate/up kernel over {reps} launches")
@@ -311,10 +322,55 @@ def main():
         "step": {"bytes_per_token": nbytes["total"], "effective_GBps": round(step_bw, 1),
                  "hbm_frac": round(step_bw / HBM_PEAK_GBS, 4), "graph_gpu_ms": round(gpu_ms, 3)},
         "verify": verify,
+        "decode_steer": steer,
         "decode_q4k": decode_q4k,
         "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
+
+
+def combine_bench(k, H, Ts, reps):
+    """Average launch time of the combine with and without steering, per token count T (graph of `reps`
+    launches, HIP events), and the algorithmic bytes each moves: k + 1 input rows, one output row and k weights
+    per token, plus the direction once for the steered form."""
+    import torch
+    from bit_quantized_moe_permute_amd import moe_combine, moe_combine_steer
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(5)
+    v = torch.randn(H, device=dev, generator=g)
+    out = {}
+    for T in Ts:
+        o = torch.randn(T * k, H, device=dev, generator=g)
+        w = torch.rand(T, k, device=dev, generator=g)
+        sh = torch.randn(T, H, device=dev, generator=g)
+        y = torch.empty(T, H, device=dev)
+        nbytes = T * ((k + 2) * H * 4 + k * 4)
+        res = {}
+        for name, fn in (("plain", lambda: moe_combine(o, w, sh, T, k, H, y)),
+                         ("steer", lambda: moe_combine_steer(o, w, sh, T, k, H, v, 1.0, y))):
+            fn()
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(gr, stream=cap):
+                    for _ in range(reps):
+                        fn()
+            torch.cuda.synchronize()
+            gr.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            b = nbytes + (H * 4 if name == "steer" else 0)
+            res[name] = {"us": round(us, 3), "GBps": round(b / (us * 1e-6) / 1e9, 1)}
+            del gr
+        out[f"T{T}"] = res
+    return out
 
 
 def prefill_bench(L, DL, reps, names):

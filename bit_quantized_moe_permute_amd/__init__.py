@@ -19,12 +19,12 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE = 0, 1, 2, 3
 DT_F32, DT_BF16 = 0, 1
 FMT_IQ2X, FMT_Q2K, FMT_Q4K = 1, 2, 3
 PATH_AUTO, PATH_GENERIC, PATH_GEMV, PATH_GEMM = 0, 1, 2, 3
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTS = [
     "moe_abi_version", "moe_last_error", "moe_weight_bytes", "moe_prepare_weights", "moe_dequantize",
     "moe_route_workspace", "moe_route", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_expert_gate_up",
-    "moe_expert_down", "moe_combine",
+    "moe_expert_down", "moe_combine", "moe_combine_steer",
 ]
 
 
@@ -77,6 +77,8 @@ def _load():
     L.moe_expert_down.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_combine.restype = ctypes.c_int
     L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
+    L.moe_combine_steer.restype = ctypes.c_int
+    L.moe_combine_steer.argtypes = [vp, vp, vp, i32, i32, i32, vp, ctypes.c_float, vp, vp]
     if L.moe_abi_version() != ABI_VERSION:
         raise ImportError(f"libmoe2bit ABI {L.moe_abi_version()} != binding ABI {ABI_VERSION}")
     return L
@@ -172,6 +174,11 @@ def moe_expert_down(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, 
 def moe_combine(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, y, stream=None):
     _check(lib.moe_combine(_ptr(slot_out), _ptr(topk_w), _ptr(shared_out), n_tokens, top_k, hidden, _ptr(y),
                            _stream(stream)))
+
+
+def moe_combine_steer(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, steer_v, steer_f, y, stream=None):
+    _check(lib.moe_combine_steer(_ptr(slot_out), _ptr(topk_w), _ptr(shared_out), n_tokens, top_k, hidden,
+                                 _ptr(steer_v), float(steer_f), _ptr(y), _stream(stream)))
 
 
 from .layer import DeviceLayer, LayerBuffers  # noqa: E402  (needs `lib` loaded)

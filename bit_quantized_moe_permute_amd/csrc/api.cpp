@@ -3,6 +3,7 @@
 // synchronizes; no C++ exception crosses the interface.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -273,6 +274,20 @@ moe_status moe_combine(const float *slot_out, const float *topk_w, const float *
         return fail(MOE_ERR_INVALID_ARG, "moe_combine: misaligned pointer");
     return from_hip(moe::launch_combine(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, y, (hipStream_t)stream),
                     "moe_combine");
+}
+
+moe_status moe_combine_steer(const float *slot_out, const float *topk_w, const float *shared_out, int32_t n_tokens,
+                             int32_t top_k, int32_t hidden, const float *steer_v, float steer_f, float *y,
+                             void *stream) {
+    if (!slot_out || !topk_w || !y || !steer_v) return fail(MOE_ERR_INVALID_ARG, "moe_combine_steer: null pointer");
+    if (n_tokens < 1 || top_k < 1 || hidden < 1) return fail(MOE_ERR_INVALID_ARG, "moe_combine_steer: bad shape");
+    if (!aligned(slot_out, 4) || !aligned(y, 4) || !aligned(topk_w, 4) || !aligned(steer_v, 4) ||
+        (shared_out && !aligned(shared_out, 4)))
+        return fail(MOE_ERR_INVALID_ARG, "moe_combine_steer: misaligned pointer");
+    if (!std::isfinite(steer_f)) return fail(MOE_ERR_INVALID_ARG, "moe_combine_steer: steering strength not finite");
+    return from_hip(moe::launch_combine_steer(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, steer_v, steer_f,
+                                              y, (hipStream_t)stream),
+                    "moe_combine_steer");
 }
 
 }  // extern "C"

@@ -61,5 +61,7 @@ hipError_t launch_ffn_gemm(const FfnArgs &a, hipStream_t st);
 // combine.hip
 hipError_t launch_combine(const float *slot_out, const float *topk_w, const float *shared_out, int T, int k, int H,
                           float *y, hipStream_t st);
+hipError_t launch_combine_steer(const float *slot_out, const float *topk_w, const float *shared_out, int T, int k,
+                                int H, const float *v, float F, float *y, hipStream_t st);
 
 }  // namespace moe

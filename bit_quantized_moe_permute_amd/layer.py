@@ -10,8 +10,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import (FMT_IQ2X, PATH_AUTO, LayerDesc, moe_combine, moe_expert_ffn, moe_expert_ffn_workspace,
-               moe_prepare_weights, moe_route, moe_route_workspace, moe_weight_bytes)
+from . import (FMT_IQ2X, PATH_AUTO, LayerDesc, moe_combine, moe_combine_steer, moe_expert_ffn,
+               moe_expert_ffn_workspace, moe_prepare_weights, moe_route, moe_route_workspace, moe_weight_bytes)
 
 
 def _u8(a: np.ndarray, device) -> torch.Tensor:
@@ -49,6 +49,18 @@ class DeviceLayer:
             self.Is = self.shared[0].shape[0]
         self.path = path
         self.desc = self.make_desc(path)
+        self.steer_v, self.steer_f = None, 0.0
+
+    def set_steering(self, v, F: float = 1.0):
+        """Directional steering of this layer's FFN output, y -= F * v * dot(v, y): v is one fp32 value per hidden
+        unit (used as given), or None to turn steering off."""
+        if v is None:
+            self.steer_v, self.steer_f = None, 0.0
+            return
+        v = np.ascontiguousarray(v, dtype=np.float32).reshape(-1)
+        if v.shape[0] != self.H:
+            raise ValueError(f"steering direction has {v.shape[0]} entries, the layer has hidden {self.H}")
+        self.steer_v, self.steer_f = torch.from_numpy(v).to(self.device), float(F)
 
     def _prepare(self, fmt, blocks, rows, cols):
         nbytes = moe_weight_bytes(fmt, self.E, rows, cols)
@@ -81,6 +93,7 @@ class DeviceLayer:
         c.w_router = self.w_router.clone()
         c.bias = None if self.bias is None else self.bias.clone()
         c.shared = None if self.shared is None else tuple(s.clone() for s in self.shared)
+        c.steer_v = None if self.steer_v is None else self.steer_v.clone()
         c.desc = c.make_desc(self.path)
         return c
 
@@ -129,12 +142,16 @@ class LayerBuffers:
 
 
 def forward(L: DeviceLayer, x: torch.Tensor, b: LayerBuffers, desc: LayerDesc | None = None, stream=None):
-    """route -> expert FFN -> combine for x [T][H] (bf16 or fp32) into b.y."""
+    """route -> expert FFN -> combine (+ steering, when the layer has a direction) for x [T][H] (bf16 or fp32)
+    into b.y."""
     T = x.shape[0]
     assert T == b.T
     moe_route(x, L.w_router, L.E, L.k, b.topk_idx, b.topk_w, b.offsets, b.perm, b.active, b.ws_route, bias=L.bias,
               logits=b.logits, stream=stream)
     moe_expert_ffn(desc or L.desc, x, b.topk_idx, b.offsets, b.perm, b.active, b.slot_out, b.shared_out, b.ws_ffn,
                    stream=stream)
-    moe_combine(b.slot_out, b.topk_w, b.shared_out, T, L.k, L.H, b.y, stream=stream)
+    if L.steer_v is None:
+        moe_combine(b.slot_out, b.topk_w, b.shared_out, T, L.k, L.H, b.y, stream=stream)
+    else:
+        moe_combine_steer(b.slot_out, b.topk_w, b.shared_out, T, L.k, L.H, L.steer_v, L.steer_f, b.y, stream=stream)
     return b.y

@@ -19,7 +19,8 @@
  *   moe_expert_ffn  the routed experts (gate/up + SwiGLU + down, per slot) and
  *                   the shared expert;
  *   moe_combine     the top-k weighted sum of the slot outputs plus the shared
- *                   output.
+ *                   output (moe_combine_steer: the same, then directional
+ *                   steering of the result).
  *
  * Conventions for every function below.
  *  - Pointers are DEVICE pointers unless the comment says "host".  The caller
@@ -61,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
     MOE_OK = 0,
@@ -203,6 +204,26 @@ moe_status moe_expert_down(const moe_layer_desc *L, const void *x, int32_t x_dt,
  */
 moe_status moe_combine(const float *slot_out, const float *topk_w, const float *shared_out, int32_t n_tokens,
                        int32_t top_k, int32_t hidden, float *y, void *stream);
+
+/*
+ * The combine above followed by directional steering of the FFN output
+ * ("DwarfStar4 / ds4.c" user report on modu-print.com, the ds4-server option
+ * listing, the FFN steering option): with the layer's direction v and strength
+ * F, every token's combined output y[t] loses F times its component along v,
+ *
+ *   y[t] <- y[t] - F * v * dot(v, y[t]).
+ *
+ * steer_v   [hidden] fp32, device; used as given (not normalised), read only.
+ * steer_f   host scalar; F = 0 gives the plain combine (up to the sign of zero).
+ * y         [n_tokens][hidden] fp32, written; must not alias any input.
+ * dot(v, y[t]) is an fp32 sum whose order is fixed per launch shape, so
+ * results are deterministic run to run.  One workgroup per token.  Returns
+ * MOE_ERR_INVALID_ARG for a NULL input or output, a bad shape, a pointer not
+ * 4-byte aligned or a non-finite steer_f.
+ */
+moe_status moe_combine_steer(const float *slot_out, const float *topk_w, const float *shared_out, int32_t n_tokens,
+                             int32_t top_k, int32_t hidden, const float *steer_v, float steer_f, float *y,
+                             void *stream);
 
 #ifdef __cplusplus
 }

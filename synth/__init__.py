@@ -17,6 +17,8 @@ Workloads (layer shapes; all inputs seeded):
   prefill   the decode layer, 512 tokens, router bias N(0,0.5) per expert.
   long      the decode layer, 11,709 tokens in 2048-token chunks, routed
             experts in 2-bit form and in a q4k (4.5 bpw) form.
+  steering  one unit-length fp32 direction per layer (normalised N(0,1)
+            draws), strength 1.
 
 Full-size routed experts (1.8 GB of blocks per layer) are drawn field by field
 ("random blocks"): every bit pattern of the formats decodes to a valid block,
@@ -38,7 +40,7 @@ BLOCK_BYTES = {FMT_IQ2X: 66, FMT_Q2K: 84, FMT_Q4K: 144}
 QK = 256
 
 # tensor ids for per-tensor random streams
-_T_X, _T_ROUTER, _T_BIAS, _T_SG, _T_SU, _T_SD, _T_G, _T_U, _T_D, _T_CB = range(1, 11)
+_T_X, _T_ROUTER, _T_BIAS, _T_SG, _T_SU, _T_SD, _T_G, _T_U, _T_D, _T_CB, _T_STEER = range(1, 12)
 
 
 def rng(seed: int, tensor: int, part: int = 0) -> np.random.Generator:
@@ -182,6 +184,12 @@ def activations(name: str, n_tokens: int, hidden: int, bf16: bool, seed: Optiona
     s = X_SEEDS[name] if seed is None else seed
     x = normal_f32(s, _T_X, (n_tokens, hidden), 1.0)
     return to_bf16_bits(x) if bf16 else x
+
+
+def steer_direction(hidden: int, seed: int = 0) -> np.ndarray:
+    """A unit-length fp32 direction [hidden] for directional steering (N(0,1) draws, normalised)."""
+    v = rng(seed, _T_STEER).standard_normal(size=hidden, dtype=np.float64)
+    return (v / np.linalg.norm(v)).astype(np.float32)
 
 
 def make_router(spec: LayerSpec | str):

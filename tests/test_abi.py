@@ -132,3 +132,15 @@ def test_prepare_and_combine_reject_bad_arguments(lib):
     g.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]
     assert g(None, vp(0x1000), None, 1, 8, 4096, vp(0x1000), None) == 1
     assert g(vp(0x1000), vp(0x1000), None, 0, 8, 4096, vp(0x1000), None) == 1
+    h = lib.moe_combine_steer
+    h.restype = ctypes.c_int
+    h.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_float, vp, vp]
+    p = vp(0x1000)
+    assert h(p, p, None, 1, 8, 4096, None, 1.0, p, None) == 1                  # no direction
+    assert "null" in _err(lib)
+    assert h(p, p, None, 1, 0, 4096, p, 1.0, p, None) == 1                     # top_k
+    assert h(p, p, None, 1, 8, 4096, vp(0x1002), 1.0, p, None) == 1           # misaligned direction
+    assert h(p, p, vp(0x1001), 1, 8, 4096, p, 1.0, p, None) == 1              # misaligned shared output
+    assert h(p, p, None, 1, 8, 4096, p, float("nan"), p, None) == 1           # strength not finite
+    assert "finite" in _err(lib)
+    assert h(p, p, None, 1, 8, 4096, p, float("inf"), p, None) == 1
