@@ -216,6 +216,23 @@ def main():
               "us_per_step": round(vwall * 1e6 / vK, 2)}
     log(f"verify: {vK} steps of 3 tokens -> {3 * vK / vwall:.0f} tokens/s, {vwall * 1e6 / vK:.1f} us/step")
 
+    # verifier micro-batches of M = 1 + drafts tokens (independent seeded tokens, same layer copies)
+    sweep = {}
+    for M in (2, 4, 8):
+        mx = torch.from_numpy(synth.activations("verify", M * vK, H, True, seed=12 + M).view(np.int16)) \
+            .view(torch.bfloat16).to(dev)
+        mbufs = [LayerBuffers.allocate(layers[0], M) for _ in range(2)]
+
+        def mstep(i, M=M, mx=mx, mbufs=mbufs):
+            b = mbufs[i % 2]
+            forward(layers[i % args.layers], mx[M * i: M * i + M], b)
+            return b.y
+
+        mwall, _ = graph_steps(mstep, vK, min(W, vK))
+        sweep[f"M{M}"] = {"tokens_per_s": round(M * vK / mwall, 1), "us_per_step": round(mwall * 1e6 / vK, 2)}
+        log(f"verify M={M}: {M * vK / mwall:.0f} tokens/s, {mwall * 1e6 / vK:.1f} us/step")
+    verify["sweep"] = sweep
+
     # directional steering of the FFN output (y -= F v (v . y)), fused into the combine
     steer_v = synth.steer_direction(H)
     for Lc in layers:

@@ -184,7 +184,7 @@ static moe::FfnArgs make_args(const moe_layer_desc *L, const void *x, int x_dt, 
 // Kernel family for this call: 1 generic, 2 gemv, 3 gemm.
 static int choose_path(const moe_layer_desc *L, const moe::FfnArgs &a) {
     if (L->path != MOE_PATH_AUTO) return L->path;
-    if (a.T <= 4 && moe::ffn_gemv_supported(a)) return MOE_PATH_GEMV;
+    if (moe::ffn_gemv_supported(a)) return MOE_PATH_GEMV;
     if (a.T > 4 && moe::ffn_gemm_supported(a)) return MOE_PATH_GEMM;
     return MOE_PATH_GENERIC;
 }
@@ -229,8 +229,9 @@ static moe_status expert_call(const char *fn, int stages, const moe_layer_desc *
     a.slot_out = slot_out; a.shared_out = shared_out; a.ws = ws; a.stages = stages;
     const int path = choose_path(L, a);
     if (path == MOE_PATH_GEMV && !(moe::ffn_gemv_supported(a)))
-        return fail(MOE_ERR_UNSUPPORTED, "%s: decode kernels need bf16 x, T <= 4 and "
-                                         "hidden in {512..4096}, supported inter/shared sizes", fn);
+        return fail(MOE_ERR_UNSUPPORTED, "%s: decode kernels need bf16 x, T <= 4 (T <= 8 with iq2x gate/up, "
+                                         "q2k down and T*k <= 64), hidden in {512..4096}, supported inter/shared "
+                                         "sizes", fn);
     if (path == MOE_PATH_GEMM && !(moe::ffn_gemm_supported(a)))
         return fail(MOE_ERR_UNSUPPORTED, "%s: grouped-GEMM kernels need bf16 x and hidden, inter, "
                                          "shared_inter multiples of 256", fn);

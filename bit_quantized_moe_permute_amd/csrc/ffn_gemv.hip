@@ -1,4 +1,4 @@
-// Decode / verify expert FFN: GEMV kernels for at most 4 tokens per expert.
+// Decode / verify expert FFN: GEMV kernels for at most 8 tokens per call.
 //
 // Each selected expert's weights are streamed once per call with 16-byte
 // lane loads.  A lane always covers the same columns, so the activations (x
@@ -373,6 +373,35 @@ __device__ __forceinline__ mf_acc_t mfma_f8f4(const mf_ab_t &a, uint4 b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, zero, 0, 4, 0, 0, 0, 0);
 }
 
+// Activation pieces of one token: thread tid converts x[8 tid .. 8 tid + 7]
+// (bf16 pairs in xv) into e4m3 hi and lo pieces at xhi/xlo[8 tid ..]; the four
+// threads of a 32-value group share the scale 2^-s, stored at xsc[tid / 4].
+__device__ __forceinline__ void x_to_pieces(uint4 xv, int tid, uint8_t *xhi, uint8_t *xlo, float *xsc) {
+    const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
+    float mx = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(w4[k] << 16)), fabsf(__uint_as_float(w4[k] & 0xFFFF0000u))));
+    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+    const int sh = mx > 0.f ? 7 - ilogbf(mx) : 0;
+    if ((tid & 3) == 0) xsc[tid >> 2] = ldexpf(1.f, -sh);
+    uint32_t hi2[2], lo2[2];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float v0 = ldexpf(__uint_as_float(w4[k] << 16), sh);
+        const float v1 = ldexpf(__uint_as_float(w4[k] & 0xFFFF0000u), sh);
+        const uint32_t hp = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+        const float r0 = v0 - __builtin_amdgcn_cvt_f32_fp8(hp, 0);
+        const float r1 = v1 - __builtin_amdgcn_cvt_f32_fp8(hp, 1);
+        const uint32_t lp = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+        if (k & 1) { hi2[k >> 1] |= (hp & 0xFFFFu) << 16; lo2[k >> 1] |= (lp & 0xFFFFu) << 16; }
+        else { hi2[k >> 1] = hp & 0xFFFFu; lo2[k >> 1] = lp & 0xFFFFu; }
+    }
+    *reinterpret_cast<uint2 *>(xhi + 8 * tid) = make_uint2(hi2[0], hi2[1]);
+    *reinterpret_cast<uint2 *>(xlo + 8 * tid) = make_uint2(lo2[0], lo2[1]);
+}
+
 // active: the active-expert list, read-only here; with uniform indices it is
 // read through the scalar cache, whose wait counter is separate from the
 // weight loads in flight.  The expert's slots come from topk_idx (T*k <= 64
@@ -434,29 +463,7 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
             if ((tid & 3) == 0) xsc[m][tid >> 2] = 0.f;
             continue;
         }
-        const uint32_t w4[4] = {xv[m].x, xv[m].y, xv[m].z, xv[m].w};
-        float mx = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(w4[k] << 16)), fabsf(__uint_as_float(w4[k] & 0xFFFF0000u))));
-        mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-        const int sh = mx > 0.f ? 7 - ilogbf(mx) : 0;
-        if ((tid & 3) == 0) xsc[m][tid >> 2] = ldexpf(1.f, -sh);
-        uint32_t hi2[2], lo2[2];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float v0 = ldexpf(__uint_as_float(w4[k] << 16), sh);
-            const float v1 = ldexpf(__uint_as_float(w4[k] & 0xFFFF0000u), sh);
-            const uint32_t hp = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
-            const float r0 = v0 - __builtin_amdgcn_cvt_f32_fp8(hp, 0);
-            const float r1 = v1 - __builtin_amdgcn_cvt_f32_fp8(hp, 1);
-            const uint32_t lp = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
-            if (k & 1) { hi2[k >> 1] |= (hp & 0xFFFFu) << 16; lo2[k >> 1] |= (lp & 0xFFFFu) << 16; }
-            else { hi2[k >> 1] = hp & 0xFFFFu; lo2[k >> 1] = lp & 0xFFFFu; }
-        }
-        *reinterpret_cast<uint2 *>(&xq[m][0][8 * tid]) = make_uint2(hi2[0], hi2[1]);
-        *reinterpret_cast<uint2 *>(&xq[m][1][8 * tid]) = make_uint2(lo2[0], lo2[1]);
+        x_to_pieces(xv[m], tid, xq[m][0], xq[m][1], xsc[m]);
     }
     if (ai >= n_active) return;                               // whole workgroup: fewer experts than launched
     // --- every token of the call is multiplied (the products hold MAXM
@@ -560,6 +567,237 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
             u += red[(((w * MF_RB + rb) * 2 + 1) * MAXM + m) * 16 + nn];
         }
         h[(int64_t)sl * I + r] = (_Float16)silu_mul(g, u);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Several tokens per call (2 <= T <= MT_MAX, T*k <= 64: the speculative
+// verifier's micro-batch).  Every selected expert is still read once per call,
+// but a workgroup multiplies only the tokens routed to its expert, found from
+// topk_idx by a ballot, two per pass (one product per K step, as for one
+// token); experts with more tokens take more passes over the weights already
+// in registers.  The shared rows loop over the tokens the same way, so register
+// use does not grow with T.
+// ---------------------------------------------------------------------------
+// Makes a register value opaque to the optimizer (an empty asm that "modifies" it), so that work derived from
+// weights held across a token loop is redone per token instead of being hoisted out of the loop, which would
+// hold every decoded weight in registers at once.
+__device__ __forceinline__ void opaque(uint32_t &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(uint4 &v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
+
+constexpr int MT_MAX = 8;
+
+__device__ __forceinline__ void routed_gateup_mt(const FfnArgs &a, const int32_t *__restrict__ active, int ai,
+                                                 int row0, _Float16 *__restrict__ h, uint32_t *cb4, uint32_t *sgn,
+                                                 uint8_t (*xq)[2][MF_MAXH], float (*xsc)[MF_MAXH / 32],
+                                                 float *red) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
+    const int n = lane & 15, qd = lane >> 4;
+    const int H = a.H, I = a.I;
+    const int k0w = wv * MF_KW;
+    const int n_active = active[0];
+    const int e = min(max(active[1 + ai], 0), a.E - 1);
+    const int n_slots = a.T * a.k;
+    const int sel_raw = a.topk_idx[min(lane, n_slots - 1)];
+    uint2 cbrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cbrow[i] = reinterpret_cast<const uint2 *>(a.codebook)[min(tid + i * (int)blockDim.x, 255)];
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t nb_row = H / MOE_QK, nb_mat = (int64_t)I * nb_row, NB = nb_mat * a.E;
+    uint4 wq[2 * MF_RB][2];
+    uint32_t wd[2 * MF_RB];
+#pragma unroll
+    for (int u = 0; u < 2 * MF_RB; ++u) {
+        const int r = min(row0 + 16 * (u >> 1) + n, I - 1);
+        const int64_t bl = (int64_t)e * nb_mat + (int64_t)r * nb_row + (k0w >> 8) + (u & 1);
+        wq[u][0] = reinterpret_cast<const uint4 *>(a.gate + bl * 64)[qd];
+        wq[u][1] = reinterpret_cast<const uint4 *>(a.up + bl * 64)[qd];
+        wd[u] = (uint32_t)reinterpret_cast<const uint16_t *>(a.gate + NB * 64)[bl] |
+                ((uint32_t)reinterpret_cast<const uint16_t *>(a.up + NB * 64)[bl] << 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = tid + i * (int)blockDim.x;
+        if (row < 256) cb4[row] = cbrow_fp4(cbrow[i].x, cbrow[i].y);
+        if (row < 256) sgn[row] = sign_spread(row & 0x7F);
+    }
+    if (ai >= n_active) return;                               // whole workgroup
+    // this expert's slots, ascending (so its tokens ascending); at most one per token
+    uint64_t rest = __ballot(lane < n_slots && sel_raw == e);
+    const int qa = n >> 2, at = (n >> 1) & 1, ap = n & 1;
+    const bool arow = (qd >> 1) == (qa & 1);
+    while (rest) {                                            // uniform: one pass per two tokens
+#pragma unroll
+        for (int u = 0; u < 2 * MF_RB; ++u) {
+            opaque(wq[u][0]);
+            opaque(wq[u][1]);
+            opaque(wd[u]);
+        }
+        const int s0 = __builtin_ffsll((long long)rest) - 1;
+        rest &= rest - 1;
+        const int s1 = rest ? __builtin_ffsll((long long)rest) - 1 : -1;
+        if (rest) rest &= rest - 1;
+        // pieces of the pass's tokens: token s0 / k in position 0, s1 / k (or nothing) in position 1
+        const uint4 xv0 = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) +
+                                                           (int64_t)(s0 / a.k) * H + 8 * tid);
+        x_to_pieces(xv0, tid, xq[0][0], xq[0][1], xsc[0]);
+        if (s1 >= 0) {
+            const uint4 xv1 = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) +
+                                                               (int64_t)(s1 / a.k) * H + 8 * tid);
+            x_to_pieces(xv1, tid, xq[1][0], xq[1][1], xsc[1]);
+        } else if ((tid & 3) == 0) {
+            xsc[1][tid >> 2] = 0.f;
+        }
+        __syncthreads();
+        // A operands [K block][K step]: row n = 4 qa + 2 at + ap holds position at, piece ap
+        const bool val = arow && (at == 0 || s1 >= 0);
+        mf_ab_t A[2][2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs) {
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (val) v = *reinterpret_cast<const uint4 *>(&xq[at][ap][k0w + 256 * b + 128 * hs + 32 * qa + 16 * (qd & 1)]);
+                const uint4 lo = qa < 2 ? v : make_uint4(0u, 0u, 0u, 0u), hi = qa < 2 ? make_uint4(0u, 0u, 0u, 0u) : v;
+                A[b][hs] = mf_ab_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+        float tot[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+#pragma unroll
+        for (int u = 0; u < 2 * MF_RB; ++u) {
+            const int b = u & 1;
+            const float dsc[2] = {f16_bits_to_f32(wd[u] & 0xFFFFu), f16_bits_to_f32(wd[u] >> 16)};
+            mf_acc_t acc[2][2];
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    const uint4 c = wq[u][f];
+                    const uint32_t lo = hs ? c.z : c.x, hi = hs ? c.w : c.y;
+                    uint4 bw;
+                    bw.x = cb4[lo & 0xFFu] | sgn[(lo >> 8) & 0xFFu];
+                    bw.y = cb4[(lo >> 16) & 0xFFu] | sgn[lo >> 24];
+                    bw.z = cb4[hi & 0xFFu] | sgn[(hi >> 8) & 0xFFu];
+                    bw.w = cb4[(hi >> 16) & 0xFFu] | sgn[hi >> 24];
+                    acc[hs][f] = mfma_f8f4(A[b][hs], bw);
+                }
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs) {
+                const int g = (k0w + 256 * b) / 32 + qd + 4 * hs;
+                const float xs[2] = {xsc[0][g], xsc[1][g]};
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    const uint4 c = wq[u][f];
+                    const uint32_t lo = hs ? c.z : c.x, hi = hs ? c.w : c.y;
+                    const float S = dsc[f] * (float)iq2x_gscale(lo, hi);
+                    const mf_acc_t &d = acc[hs][f];
+                    tot[f][0] = __fmaf_rn(S * xs[0], d[0] + d[1], tot[f][0]);
+                    tot[f][1] = __fmaf_rn(S * xs[1], d[2] + d[3], tot[f][1]);
+                }
+            }
+            if (b == 1) {
+                const int rb = u >> 1;
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        float v = tot[f][m];
+                        v += __shfl_xor(v, 16, 64);
+                        v += __shfl_xor(v, 32, 64);
+                        if (qd == 0) red[(((wv * MF_RB + rb) * 2 + f) * 2 + m) * 16 + n] = v;
+                        tot[f][m] = 0.f;
+                    }
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < MF_RB * 2 * 16; i += blockDim.x) {
+            const int nn = i & 15, m = (i >> 4) & 1, rb = i >> 5;
+            const int r = row0 + 16 * rb + nn, sl = m ? s1 : s0;
+            if (sl < 0 || r >= I) continue;
+            float g = 0.f, u = 0.f;
+            for (int w = 0; w < nw; ++w) {
+                g += red[(((w * MF_RB + rb) * 2 + 0) * 2 + m) * 16 + nn];
+                u += red[(((w * MF_RB + rb) * 2 + 1) * 2 + m) * 16 + nn];
+            }
+            h[(int64_t)sl * I + r] = (_Float16)silu_mul(g, u);
+        }
+        __syncthreads();                                       // LDS pieces and sums are reused by the next pass
+    }
+}
+
+// Shared gate/up rows for every token of the call, one token at a time against
+// the row's weights held in registers.
+template <int LPR, int CPL, int NR>
+__device__ void shared_gateup_mt(const FfnArgs &a, int row0, float *__restrict__ hs) {
+    constexpr int RPI = 64 / LPR;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int cp = lane % LPR, rsub = lane / LPR;
+    const int H = a.H, Is = a.Is;
+    uint4 gq[NR][CPL], uq[NR][CPL];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        const int r = min(row0 + (wv * NR + j) * RPI + rsub, Is - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            gq[j][i] = *reinterpret_cast<const uint4 *>(a.sg + (int64_t)r * H + 8 * (cp + LPR * i));
+            uq[j][i] = *reinterpret_cast<const uint4 *>(a.su + (int64_t)r * H + 8 * (cp + LPR * i));
+        }
+    }
+#pragma unroll 1
+    for (int t = 0; t < a.T; ++t) {
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                opaque(gq[j][i]);
+                opaque(uq[j][i]);
+            }
+        uint32_t xr[CPL][4];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + (int64_t)t * H +
+                                                            8 * (cp + LPR * i));
+            xr[i][0] = u.x; xr[i][1] = u.y; xr[i][2] = u.z; xr[i][3] = u.w;
+        }
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            float ga = 0.f, ua = 0.f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const uint32_t g4[4] = {gq[j][i].x, gq[j][i].y, gq[j][i].z, gq[j][i].w};
+                const uint32_t u4[4] = {uq[j][i].x, uq[j][i].y, uq[j][i].z, uq[j][i].w};
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const bf16x2_t xv = __builtin_bit_cast(bf16x2_t, xr[i][v]);
+                    ga = dot2_bf16(__builtin_bit_cast(bf16x2_t, g4[v]), xv, ga);
+                    ua = dot2_bf16(__builtin_bit_cast(bf16x2_t, u4[v]), xv, ua);
+                }
+            }
+            const float g = row_sum<LPR>(ga), u = row_sum<LPR>(ua);
+            const int r = row0 + (wv * NR + j) * RPI + rsub;
+            if (cp == 0 && r < Is) hs[(int64_t)t * Is + r] = silu_mul(g, u);
+        }
+    }
+}
+
+template <int SLPR, int SCPL>
+__global__ __launch_bounds__(512) void k_gemv_gateup_mt(FfnArgs a, const int32_t *__restrict__ active,
+                                                         int wgs_per_expert, int n_routed_wgs,
+                                                         _Float16 *__restrict__ h, float *__restrict__ hs) {
+    __shared__ uint32_t cb4[256], sgn[256];
+    __shared__ __attribute__((aligned(16))) uint8_t xq[2][2][MF_MAXH];
+    __shared__ float xsc[2][MF_MAXH / 32];
+    __shared__ float red[(MF_MAXH / MF_KW) * MF_RB * 2 * 2 * 16];
+    const int bid = blockIdx.x;
+    if (bid < n_routed_wgs) {
+        routed_gateup_mt(a, active, bid / wgs_per_expert, (bid % wgs_per_expert) * (16 * MF_RB), h, cb4, sgn, xq,
+                         xsc, red);
+    } else {
+        constexpr int SNR = shared_nr<SCPL>();
+        const int rows = (int)(blockDim.x >> 6) * SNR * (64 / SLPR);
+        shared_gateup_mt<SLPR, SCPL, SNR>(a, (bid - n_routed_wgs) * rows, hs);
     }
 }
 
@@ -880,6 +1118,127 @@ __global__ __launch_bounds__(256) void k_gemv_down(FfnArgs a, int wgs_per_expert
     }
 }
 
+// Several tokens per call: the expert's rows stay in registers and its tokens
+// (from the permutation) are taken one at a time; the shared rows loop over
+// every token of the call the same way.
+template <int LPR, int CPL, int NR>
+__device__ void routed_down_mt(const FfnArgs &a, int e, int o0, int ne, int row0, const _Float16 *__restrict__ h) {
+    constexpr int RPI = 64 / LPR;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int cp = lane % LPR, rsub = lane / LPR;
+    const int H = a.H, I = a.I;
+    const int64_t nb_row = I / MOE_QK, nb_mat = (int64_t)H * nb_row, NB = nb_mat * a.E;
+    const uint8_t *Q = a.down;
+    const uint8_t *S = a.down + NB * 64;
+    const uint32_t *D = reinterpret_cast<const uint32_t *>(a.down + NB * 80);
+    uint4 q[NR][CPL];
+    uint32_t sm[NR][CPL], dd[NR][CPL];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        const int r = min(row0 + (wv * NR + j) * RPI + rsub, H - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int ch = cp + LPR * i;
+            const int64_t bl = (int64_t)e * nb_mat + (int64_t)r * nb_row + (ch >> 2);
+            q[j][i] = *reinterpret_cast<const uint4 *>(Q + bl * 64 + (ch & 3) * 16);
+            sm[j][i] = *reinterpret_cast<const uint32_t *>(S + bl * 16 + (ch & 3) * 4);
+            dd[j][i] = D[bl];
+        }
+    }
+#pragma unroll 1
+    for (int m = 0; m < ne; ++m) {
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                opaque(q[j][i]);
+                opaque(sm[j][i]);
+                opaque(dd[j][i]);
+            }
+        Tokens<1> tk;
+        tk.n = 1;
+        tk.slot[0] = a.perm[o0 + m];
+        tk.tok[0] = tk.slot[0] / a.k;
+        uint32_t hr[CPL][1][32];
+        float hsum[CPL][1][4];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) load_h_chunk<1>(h, I, tk, cp + LPR * i, hr[i], hsum[i]);
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            float acc[1] = {0.f};
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) q2k_chunk<1>(q[j][i], sm[j][i], dd[j][i], hr[i], hsum[i], acc);
+            const float o = row_sum<LPR>(acc[0]);
+            const int r = row0 + (wv * NR + j) * RPI + rsub;
+            if (cp == 0 && r < H) a.slot_out[(int64_t)tk.slot[0] * H + r] = o;
+        }
+    }
+}
+
+template <int LPR, int CPL, int NR>
+__device__ void shared_down_mt(const FfnArgs &a, int row0, const float *__restrict__ hs) {
+    constexpr int RPI = 64 / LPR;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int cp = lane % LPR, rsub = lane / LPR;
+    const int H = a.H, Is = a.Is;
+    uint4 q[NR][CPL];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        const int r = min(row0 + (wv * NR + j) * RPI + rsub, H - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            q[j][i] = *reinterpret_cast<const uint4 *>(a.sd + (int64_t)r * Is + 8 * (cp + LPR * i));
+    }
+#pragma unroll 1
+    for (int t = 0; t < a.T; ++t) {
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) opaque(q[j][i]);
+        float hr[CPL][8];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const float4 *p = reinterpret_cast<const float4 *>(hs + (int64_t)t * Is + 8 * (cp + LPR * i));
+            const float4 u = p[0], v = p[1];
+            hr[i][0] = u.x; hr[i][1] = u.y; hr[i][2] = u.z; hr[i][3] = u.w;
+            hr[i][4] = v.x; hr[i][5] = v.y; hr[i][6] = v.z; hr[i][7] = v.w;
+        }
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const uint32_t w4[4] = {q[j][i].x, q[j][i].y, q[j][i].z, q[j][i].w};
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    acc = __fmaf_rn(__uint_as_float(w4[v] << 16), hr[i][2 * v], acc);
+                    acc = __fmaf_rn(__uint_as_float(w4[v] & 0xFFFF0000u), hr[i][2 * v + 1], acc);
+                }
+            }
+            const float o = row_sum<LPR>(acc);
+            const int r = row0 + (wv * NR + j) * RPI + rsub;
+            if (cp == 0 && r < H) a.shared_out[(int64_t)t * H + r] = o;
+        }
+    }
+}
+
+template <int LPR, int CPL, int SLPR, int SCPL, int NR, int SNR>
+__global__ __launch_bounds__(256) void k_gemv_down_mt(FfnArgs a, int wgs_per_expert, int n_routed_wgs,
+                                                       const _Float16 *__restrict__ h, const float *__restrict__ hs) {
+    const int bid = blockIdx.x;
+    if (bid < n_routed_wgs) {
+        const int ai = bid / wgs_per_expert;
+        if (ai >= a.active[0]) return;
+        const int e = a.active[1 + ai];
+        const int o0 = a.offsets[e];
+        constexpr int ROWS = WAVES * NR * (64 / LPR);
+        routed_down_mt<LPR, CPL, NR>(a, e, o0, a.offsets[e + 1] - o0, (bid % wgs_per_expert) * ROWS, h);
+    } else {
+        constexpr int ROWS = WAVES * SNR * (64 / SLPR);
+        shared_down_mt<SLPR, SCPL, SNR>(a, (bid - n_routed_wgs) * ROWS, hs);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -950,6 +1309,60 @@ hipError_t run_down(const FfnArgs &a, int max_active, const _Float16 *h, const f
     return hipGetLastError();
 }
 
+template <int SLPR, int SCPL>
+hipError_t run_gateup_mt(const FfnArgs &a, int max_active, _Float16 *h, float *hs, hipStream_t st) {
+    const int threads = a.H / 8;
+    const int wpe = a.I / (16 * MF_RB);
+    const int nr = max_active * wpe;
+    int ns = 0;
+    if (a.Is > 0) {
+        const int srows = (threads / 64) * shared_nr<SCPL>() * (64 / SLPR);
+        ns = (a.Is + srows - 1) / srows;
+    }
+    hipLaunchKernelGGL((k_gemv_gateup_mt<SLPR, SCPL>), dim3(nr + ns), dim3(threads), 0, st, a, a.active, wpe, nr, h,
+                       hs);
+    return hipGetLastError();
+}
+
+template <int LPR, int SLPR, int SCPL>
+hipError_t run_down_mt(const FfnArgs &a, int max_active, const _Float16 *h, const float *hs, hipStream_t st) {
+    constexpr int NRD = nr_down<1>(), SNR = shared_nr_down<SCPL, 1>();
+    const int rows = WAVES * NRD * (64 / LPR);
+    const int wpe = (a.H + rows - 1) / rows;
+    const int nr = max_active * wpe;
+    int ns = 0;
+    if (a.Is > 0) {
+        const int srows = WAVES * SNR * (64 / SLPR);
+        ns = (a.H + srows - 1) / srows;
+    }
+    hipLaunchKernelGGL((k_gemv_down_mt<LPR, 1, SLPR, SCPL, NRD, SNR>), dim3(nr + ns), dim3(256), 0, st, a, wpe, nr, h,
+                       hs);
+    return hipGetLastError();
+}
+
+// iq2x gate/up and q2k down, a shared expert of the routed size or none, 2 <= T <= MT_MAX, T*k <= 64
+bool mt_ok(const FfnArgs &a) {
+    return a.T >= 2 && a.T <= MT_MAX && a.fmt_d == FMT_Q2K && gateup_mfma_ok(a) && (a.Is == a.I || a.Is == 0);
+}
+
+hipError_t dispatch_mt(const FfnArgs &a, _Float16 *h, float *hs, hipStream_t st) {
+    const int max_active = min(a.T * a.k, a.E);
+    hipError_t e = hipErrorInvalidValue;
+    if (a.stages & STAGE_GATE_UP) {
+        if (a.H == 4096) e = run_gateup_mt<64, 8>(a, max_active, h, hs, st);
+        else if (a.H == 2048) e = run_gateup_mt<64, 4>(a, max_active, h, hs, st);
+        else if (a.H == 1024) e = run_gateup_mt<64, 2>(a, max_active, h, hs, st);
+        else if (a.H == 512) e = run_gateup_mt<64, 1>(a, max_active, h, hs, st);
+        if (e != hipSuccess) return e;
+    }
+    if (!(a.stages & STAGE_DOWN)) return hipSuccess;
+    if (a.I == 2048) return run_down_mt<32, 64, 4>(a, max_active, h, hs, st);
+    if (a.I == 1024) return run_down_mt<16, 64, 2>(a, max_active, h, hs, st);
+    if (a.I == 512) return run_down_mt<8, 64, 1>(a, max_active, h, hs, st);
+    if (a.I == 256) return run_down_mt<4, 32, 1>(a, max_active, h, hs, st);
+    return hipErrorInvalidValue;
+}
+
 template <int MAXM>
 hipError_t dispatch(const FfnArgs &a, _Float16 *h, float *hs, hipStream_t st) {
     const int max_active = min(a.T * a.k, a.E);
@@ -992,7 +1405,8 @@ hipError_t dispatch(const FfnArgs &a, _Float16 *h, float *hs, hipStream_t st) {
 namespace moe {
 
 bool ffn_gemv_supported(const FfnArgs &a) {
-    if (!a.x_bf16 || a.T > 4) return false;
+    if (!a.x_bf16 || a.T > MT_MAX) return false;
+    if (a.T > 4 && !mt_ok(a)) return false;
     if (a.fmt_gu != FMT_IQ2X && a.fmt_gu != FMT_Q4K) return false;
     if (a.fmt_d != FMT_Q2K && a.fmt_d != FMT_Q4K) return false;
     if (!(a.H == 4096 || a.H == 2048 || a.H == 1024 || a.H == 512)) return false;
@@ -1014,6 +1428,7 @@ hipError_t launch_ffn_gemv(const FfnArgs &a, hipStream_t st) {
     size_t hb = ((size_t)a.T * a.k * a.I * sizeof(_Float16) + 255) / 256 * 256;
     float *hs = reinterpret_cast<float *>(static_cast<char *>(a.ws) + hb);
     if (a.T == 1) return dispatch<1>(a, h, hs, st);
+    if (mt_ok(a)) return dispatch_mt(a, h, hs, st);
     return dispatch<4>(a, h, hs, st);
 }
 

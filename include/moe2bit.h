@@ -172,8 +172,9 @@ size_t moe_expert_ffn_workspace(const moe_layer_desc *L, int32_t n_tokens);
  *   shared_out [T][H] fp32: FFN_shared(x[t]); NULL iff L->shared_inter == 0.
  *   ws: workspace of at least moe_expert_ffn_workspace(L, T) bytes.
  * Numerics: decoded weights are exact; products accumulate in fp32.  The
- * SwiGLU output h of routed slots is kept in fp16 (decode kernels, T <= 4, and
- * grouped-GEMM kernels, T > 4) or fp32 (generic kernels); the shared expert's
+ * SwiGLU output h of routed slots is kept in fp16 (decode kernels: T <= 4, or
+ * T <= 8 for iq2x gate/up with q2k down and T*k <= 64; grouped-GEMM kernels
+ * above that) or fp32 (generic kernels); the shared expert's
  * h in fp32 (decode, generic) or as a bf16 hi + lo pair (grouped GEMM).  The
  * grouped-GEMM kernels read x as fp16 (exact for bf16 values in fp16 range).
  */

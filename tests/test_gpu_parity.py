@@ -223,8 +223,11 @@ LAYER_CASES = [
     ("tiny", 4, 0), ("small", 1, 0), ("small", 3, 0), ("small", 4, 0), ("small", 1, 1), ("small", 37, 1),
     ("mid", 2, 0), ("mid", 9, 1), ("mid_fp32", 3, 0),
     # grouped-GEMM kernels: auto path above 4 tokens, and forced at the degenerate sizes
-    ("small", 5, 0), ("small", 37, 0), ("small", 1, 3), ("small", 3, 3), ("mid", 70, 0), ("mid", 130, 0),
+    ("small", 37, 0), ("small", 1, 3), ("small", 3, 3), ("small", 5, 3), ("mid", 70, 0), ("mid", 130, 0),
     ("mid", 300, 0),
+    # several tokens per call on the decode kernels (speculative verify micro-batch, up to 8 tokens, T*k <= 64)
+    ("small", 2, 0), ("small", 5, 0), ("small", 6, 0), ("small", 8, 0), ("small", 8, 2), ("mid", 5, 0),
+    ("mid", 8, 0), ("small", 9, 0),
     # q4k routed experts (4.5 bpw) and mixed formats: decode sizes and grouped GEMM
     ("small_q4k", 1, 0), ("small_q4k", 3, 0), ("small_q4k", 4, 0), ("small_q4k", 3, 1), ("small_q4k", 37, 0),
     ("small_q4k", 3, 3), ("small_q4k", 70, 0),
@@ -249,7 +252,8 @@ def test_layer_matches_oracle(m, name, T, path):
     assert err.max() <= TOL
 
 
-@pytest.mark.parametrize("name,T", [("decode", 1), ("decode", 3), ("long_q4k", 1), ("long_q4k", 3)])
+@pytest.mark.parametrize("name,T", [("decode", 1), ("decode", 3), ("decode", 8), ("long_q4k", 1),
+                                    ("long_q4k", 3)])
 def test_decode_layer_full_size(m, name, T):
     """Full-size decode layer (hidden 4096, 256 experts, top-8, intermediate
     2048, bf16 shared expert), 2-bit or q4k routed experts, on several
@@ -266,6 +270,24 @@ def test_decode_layer_full_size(m, name, T):
         err = rel_l2_rows(got["y"], ref["y"])
         note(f"  max per-token rel L2 = {err.max():.3e}")
         assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("name,T", [("small", 8), ("mid", 6), ("decode", 8)])
+def test_verify_batch_of_one_repeated_token(m, name, T):
+    """T copies of one token: every selected expert gets all T tokens (T / 2 passes over its weights in the
+    several-token kernels); every row must match the oracle's single-token output."""
+    note(f"repeated token {name} T={T}")
+    L = _layer(name)
+    sp = L.spec
+    x1 = synth.activations(name, 1, sp.hidden, sp.x_bf16, seed=907)
+    x = np.repeat(x1, T, axis=0)
+    got = _run_layer(m, L, x, 0)
+    ref = _oracle_layer(L, x1)
+    assert np.array_equal(got["topk_idx"], np.repeat(ref["topk_idx"], T, axis=0))
+    err = rel_l2_rows(got["y"], np.repeat(ref["y"], T, axis=0))
+    note(f"  max per-token rel L2 = {err.max():.3e}")
+    assert err.max() <= TOL
+    assert np.array_equal(got["y"], np.repeat(got["y"][:1], T, axis=0))
 
 
 @pytest.mark.parametrize("name,T,chunk", [("prefill", 512, 512), ("long", 2048, 2048), ("long", 2600, 2048),
