@@ -212,9 +212,9 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t *__restrict__ to
 }
 
 // ---------------------------------------------------------------------------
-// Small batches (T <= 4: decode and verify).  Two launches instead of three.
+// Small batches (T <= 8: decode and verify).  Two launches instead of three.
 // ---------------------------------------------------------------------------
-constexpr int SMALL_T = 4;
+constexpr int SMALL_T = 8;
 
 // One wave per (expert, token), grid (E/4, T).  Lane p holds partial p and
 // issues all its H/64 loads before the first multiply, so the latency of the
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void k_router_logits_small(const void *__restr
     }
 }
 
-// Top-k, weights and permutation for T <= 4 tokens in one workgroup of 1024
+// Top-k, weights and permutation for T <= 8 tokens in one workgroup of 1024
 // threads.  Expert e of token t carries the key (orderable logit bits, then
 // 255 - e): a larger key is a larger logit, ties going to the lower index, and
 // keys are distinct.  The rank of e is the number of larger keys, counted in
@@ -259,17 +259,17 @@ __global__ __launch_bounds__(1024) void k_select_small(const float *__restrict__
                                                        int32_t *__restrict__ active) {
     __shared__ float lg[SMALL_T][256];
     __shared__ __attribute__((aligned(16))) unsigned long long key[SMALL_T][256];
-    __shared__ int part[4][SMALL_T][256];
+    __shared__ uint8_t part[4][SMALL_T][256];                              // at most 64 larger keys per quarter
     __shared__ int sel[SMALL_T * 256];
     __shared__ double ex[SMALL_T][256];
     __shared__ int cnt[256];
     const int tid = threadIdx.x, e = tid & 255, q = tid >> 8;
-    if (q < T) {
-        const float l = e < E ? logits[q * E + e] : 0.f;
-        lg[q][e] = l;
+    for (int t = q; t < T; t += 4) {
+        const float l = e < E ? logits[t * E + e] : 0.f;
+        lg[t][e] = l;
         const uint32_t u = __float_as_uint(l + 0.0f);                       // -0 compares equal to +0
         const uint32_t ord = u ^ ((u >> 31) ? 0xFFFFFFFFu : 0x80000000u);
-        key[q][e] = e < E ? (((unsigned long long)ord << 32) | (uint32_t)(255 - e)) : 0ull;
+        key[t][e] = e < E ? (((unsigned long long)ord << 32) | (uint32_t)(255 - e)) : 0ull;
     }
     __syncthreads();
     for (int t = 0; t < T; ++t) {
@@ -281,12 +281,12 @@ __global__ __launch_bounds__(1024) void k_select_small(const float *__restrict__
             const ulonglong2 u = row[o2];
             r += (u.x > me ? 1 : 0) + (u.y > me ? 1 : 0);
         }
-        part[q][t][e] = r;
+        part[q][t][e] = (uint8_t)r;
     }
     __syncthreads();
-    if (q < T && e < E) {
-        const int r = part[0][q][e] + part[1][q][e] + part[2][q][e] + part[3][q][e];
-        if (r < k) sel[q * k + r] = e;
+    for (int t = q; t < T && e < E; t += 4) {
+        const int r = part[0][t][e] + part[1][t][e] + part[2][t][e] + part[3][t][e];
+        if (r < k) sel[t * k + r] = e;
     }
     __syncthreads();
     const int S = T * k;

@@ -121,8 +121,8 @@ def _check_route(m, x, w_router, E, k, bias=None):
 
 
 ROUTE_CASES = [
-    ("tiny", 4), ("small", 1), ("small", 3), ("small", 37), ("mid", 70), ("decode", 1), ("decode", 3),
-    ("decode", 64), ("prefill", 512), ("long", 2048), ("long", 2500),
+    ("tiny", 4), ("small", 1), ("small", 3), ("small", 8), ("small", 37), ("mid", 6), ("mid", 70), ("decode", 1),
+    ("decode", 3), ("decode", 5), ("decode", 8), ("decode", 9), ("decode", 64), ("prefill", 512), ("long", 2048), ("long", 2500),
 ]
 
 
@@ -136,7 +136,7 @@ def test_route_matches_oracle(m, name, T):
 
 
 @pytest.mark.parametrize("k", [1, 16])
-@pytest.mark.parametrize("T", [1, 4, 9])
+@pytest.mark.parametrize("T", [1, 4, 8, 9])
 def test_route_k_extremes(m, k, T):
     note(f"route k={k} T={T}")
     wr, _ = synth.make_router("small")
@@ -144,7 +144,7 @@ def test_route_k_extremes(m, k, T):
     _check_route(m, x, wr, 16, k)
 
 
-@pytest.mark.parametrize("T", [1, 3, 5])
+@pytest.mark.parametrize("T", [1, 3, 5, 8])
 def test_route_zero_input_ties(m, T):
     note(f"route zero input T={T}")
     wr, _ = synth.make_router("small")
@@ -155,15 +155,18 @@ def test_route_zero_input_ties(m, T):
 
 
 def test_route_full_size_decode_tokens(m):
-    """The decode router (4096 x 256, bf16) on 64 separate one-token calls and 16 three-token calls."""
+    """The decode router (4096 x 256, bf16) on 64 separate one-token calls, 16 three-token calls and 8
+    eight-token calls."""
     sp = synth.SPECS["decode"]
     wr, _ = synth.make_router(sp)
-    x = synth.activations("decode", 112, sp.hidden, True, seed=977)
+    x = synth.activations("decode", 176, sp.hidden, True, seed=977)
     for i in range(64):
         _check_route(m, x[i:i + 1], wr, sp.n_experts, sp.top_k)
     for i in range(16):
         _check_route(m, x[64 + 3 * i: 67 + 3 * i], wr, sp.n_experts, sp.top_k)
-    note("route decode tokens: 64 x T=1, 16 x T=3")
+    for i in range(8):
+        _check_route(m, x[112 + 8 * i: 120 + 8 * i], wr, sp.n_experts, sp.top_k)
+    note("route decode tokens: 64 x T=1, 16 x T=3, 8 x T=8")
 
 
 def test_route_summation_order_golden(m):
