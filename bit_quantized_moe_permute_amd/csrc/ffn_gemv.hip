@@ -602,6 +602,19 @@ __device__ __forceinline__ void routed_gateup_mt(const FfnArgs &a, const int32_t
     uint2 cbrow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) cbrow[i] = reinterpret_cast<const uint2 *>(a.codebook)[min(tid + i * (int)blockDim.x, 255)];
+    // this expert's slots, ascending (so its tokens ascending; at most one slot per token).  They are
+    // resolved before the weights are requested, so that the first pass's activations are requested ahead
+    // of the weights and arrive first.
+    uint64_t rest = __ballot(lane < n_slots && sel_raw == e);
+    const uint16_t *xb = static_cast<const uint16_t *>(a.x);
+    int s0 = rest ? __builtin_ffsll((long long)rest) - 1 : 0;
+    int s1 = -1;
+    {
+        const uint64_t r1 = rest & (rest - 1);
+        if (r1) s1 = __builtin_ffsll((long long)r1) - 1;
+    }
+    const uint4 xv0 = *reinterpret_cast<const uint4 *>(xb + (int64_t)(s0 / a.k) * H + 8 * tid);
+    const uint4 xv1 = *reinterpret_cast<const uint4 *>(xb + (int64_t)((s1 >= 0 ? s1 : s0) / a.k) * H + 8 * tid);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -625,10 +638,12 @@ __device__ __forceinline__ void routed_gateup_mt(const FfnArgs &a, const int32_t
         if (row < 256) sgn[row] = sign_spread(row & 0x7F);
     }
     if (ai >= n_active) return;                               // whole workgroup
-    // this expert's slots, ascending (so its tokens ascending); at most one per token
-    uint64_t rest = __ballot(lane < n_slots && sel_raw == e);
+    x_to_pieces(xv0, tid, xq[0][0], xq[0][1], xsc[0]);
+    if (s1 >= 0) x_to_pieces(xv1, tid, xq[1][0], xq[1][1], xsc[1]);
+    else if ((tid & 3) == 0) xsc[1][tid >> 2] = 0.f;
     const int qa = n >> 2, at = (n >> 1) & 1, ap = n & 1;
     const bool arow = (qd >> 1) == (qa & 1);
+    bool first = true;
     while (rest) {                                            // uniform: one pass per two tokens
 #pragma unroll
         for (int u = 0; u < 2 * MF_RB; ++u) {
@@ -636,21 +651,23 @@ __device__ __forceinline__ void routed_gateup_mt(const FfnArgs &a, const int32_t
             opaque(wq[u][1]);
             opaque(wd[u]);
         }
-        const int s0 = __builtin_ffsll((long long)rest) - 1;
+        s0 = __builtin_ffsll((long long)rest) - 1;
         rest &= rest - 1;
-        const int s1 = rest ? __builtin_ffsll((long long)rest) - 1 : -1;
+        s1 = rest ? __builtin_ffsll((long long)rest) - 1 : -1;
         if (rest) rest &= rest - 1;
-        // pieces of the pass's tokens: token s0 / k in position 0, s1 / k (or nothing) in position 1
-        const uint4 xv0 = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) +
-                                                           (int64_t)(s0 / a.k) * H + 8 * tid);
-        x_to_pieces(xv0, tid, xq[0][0], xq[0][1], xsc[0]);
-        if (s1 >= 0) {
-            const uint4 xv1 = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) +
-                                                               (int64_t)(s1 / a.k) * H + 8 * tid);
-            x_to_pieces(xv1, tid, xq[1][0], xq[1][1], xsc[1]);
-        } else if ((tid & 3) == 0) {
-            xsc[1][tid >> 2] = 0.f;
+        // pieces of the pass's tokens: token s0 / k in position 0, s1 / k (or nothing) in position 1 (the
+        // first pass's were made above, while the weights streamed in)
+        if (!first) {
+            const uint4 v0 = *reinterpret_cast<const uint4 *>(xb + (int64_t)(s0 / a.k) * H + 8 * tid);
+            x_to_pieces(v0, tid, xq[0][0], xq[0][1], xsc[0]);
+            if (s1 >= 0) {
+                const uint4 v1 = *reinterpret_cast<const uint4 *>(xb + (int64_t)(s1 / a.k) * H + 8 * tid);
+                x_to_pieces(v1, tid, xq[1][0], xq[1][1], xsc[1]);
+            } else if ((tid & 3) == 0) {
+                xsc[1][tid >> 2] = 0.f;
+            }
         }
+        first = false;
         __syncthreads();
         // A operands [K block][K step]: row n = 4 qa + 2 at + ap holds position at, piece ap
         const bool val = arow && (at == 0 || s1 >= 0);
@@ -1121,6 +1138,26 @@ __global__ __launch_bounds__(256) void k_gemv_down(FfnArgs a, int wgs_per_expert
 // Several tokens per call: the expert's rows stay in registers and its tokens
 // (from the permutation) are taken one at a time; the shared rows loop over
 // every token of the call the same way.
+// NR rows of one routed expert (decoded weights q, sm, dd) against one slot's h.
+template <int LPR, int CPL, int NR>
+__device__ __forceinline__ void down_rows_one(const FfnArgs &a, const uint4 (&q)[NR][CPL],
+                                              const uint32_t (&sm)[NR][CPL], const uint32_t (&dd)[NR][CPL],
+                                              const uint32_t (&hr)[CPL][1][32], const float (&hsum)[CPL][1][4],
+                                              int slot, int row0) {
+    constexpr int RPI = 64 / LPR;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int cp = lane % LPR, rsub = lane / LPR;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        float acc[1] = {0.f};
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) q2k_chunk<1>(q[j][i], sm[j][i], dd[j][i], hr[i], hsum[i], acc);
+        const float o = row_sum<LPR>(acc[0]);
+        const int r = row0 + (wv * NR + j) * RPI + rsub;
+        if (cp == 0 && r < a.H) a.slot_out[(int64_t)slot * a.H + r] = o;
+    }
+}
+
 template <int LPR, int CPL, int NR>
 __device__ void routed_down_mt(const FfnArgs &a, int e, int o0, int ne, int row0, const _Float16 *__restrict__ h) {
     constexpr int RPI = 64 / LPR;
@@ -1128,6 +1165,15 @@ __device__ void routed_down_mt(const FfnArgs &a, int e, int o0, int ne, int row0
     const int cp = lane % LPR, rsub = lane / LPR;
     const int H = a.H, I = a.I;
     const int64_t nb_row = I / MOE_QK, nb_mat = (int64_t)H * nb_row, NB = nb_mat * a.E;
+    // the first token's h is requested ahead of the weights, so that it arrives first
+    Tokens<1> tk;
+    tk.n = 1;
+    tk.slot[0] = a.perm[o0];
+    tk.tok[0] = tk.slot[0] / a.k;
+    uint32_t hr[CPL][1][32];
+    float hsum[CPL][1][4];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) load_h_chunk<1>(h, I, tk, cp + LPR * i, hr[i], hsum[i]);
     const uint8_t *Q = a.down;
     const uint8_t *S = a.down + NB * 64;
     const uint32_t *D = reinterpret_cast<const uint32_t *>(a.down + NB * 80);
@@ -1145,8 +1191,9 @@ __device__ void routed_down_mt(const FfnArgs &a, int e, int o0, int ne, int row0
             dd[j][i] = D[bl];
         }
     }
+    down_rows_one<LPR, CPL, NR>(a, q, sm, dd, hr, hsum, tk.slot[0], row0);
 #pragma unroll 1
-    for (int m = 0; m < ne; ++m) {
+    for (int m = 1; m < ne; ++m) {
 #pragma unroll
         for (int j = 0; j < NR; ++j)
 #pragma unroll
@@ -1155,23 +1202,15 @@ __device__ void routed_down_mt(const FfnArgs &a, int e, int o0, int ne, int row0
                 opaque(sm[j][i]);
                 opaque(dd[j][i]);
             }
-        Tokens<1> tk;
-        tk.n = 1;
-        tk.slot[0] = a.perm[o0 + m];
-        tk.tok[0] = tk.slot[0] / a.k;
-        uint32_t hr[CPL][1][32];
-        float hsum[CPL][1][4];
+        Tokens<1> tm;
+        tm.n = 1;
+        tm.slot[0] = a.perm[o0 + m];
+        tm.tok[0] = tm.slot[0] / a.k;
+        uint32_t hm[CPL][1][32];
+        float sm_h[CPL][1][4];
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) load_h_chunk<1>(h, I, tk, cp + LPR * i, hr[i], hsum[i]);
-#pragma unroll
-        for (int j = 0; j < NR; ++j) {
-            float acc[1] = {0.f};
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) q2k_chunk<1>(q[j][i], sm[j][i], dd[j][i], hr[i], hsum[i], acc);
-            const float o = row_sum<LPR>(acc[0]);
-            const int r = row0 + (wv * NR + j) * RPI + rsub;
-            if (cp == 0 && r < H) a.slot_out[(int64_t)tk.slot[0] * H + r] = o;
-        }
+        for (int i = 0; i < CPL; ++i) load_h_chunk<1>(h, I, tm, cp + LPR * i, hm[i], sm_h[i]);
+        down_rows_one<LPR, CPL, NR>(a, q, sm, dd, hm, sm_h, tm.slot[0], row0);
     }
 }
 

@@ -246,59 +246,114 @@ __global__ __launch_bounds__(256) void k_router_logits_small(const void *__restr
     }
 }
 
+// max(m, m of the lane that DPP control CTRL reads), 64-bit; every CTRL used here gives every lane a source
+template <int CTRL> __device__ __forceinline__ unsigned long long max_dpp(unsigned long long m) {
+    const int lo = (int)(uint32_t)m, hi = (int)(uint32_t)(m >> 32);
+    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
+    const unsigned long long o = ((unsigned long long)ohi << 32) | olo;
+    return o > m ? o : m;
+}
+
+__device__ __forceinline__ unsigned long long lane_u64(unsigned long long m, int l) {
+    return ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(m >> 32), l) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)m, l);
+}
+
+// Wave-wide maximum of a 64-bit value: within each row of 16 lanes by DPP (quad swaps 1 and 2, half-row
+// mirror, row mirror), then across the four rows from one lane of each.
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long m) {
+    m = max_dpp<0xB1>(m);          // quad_perm [1,0,3,2]
+    m = max_dpp<0x4E>(m);          // quad_perm [2,3,0,1]
+    m = max_dpp<0x141>(m);         // row_half_mirror
+    m = max_dpp<0x140>(m);         // row_mirror
+    const unsigned long long a = lane_u64(m, 0), b = lane_u64(m, 16), c = lane_u64(m, 32), d = lane_u64(m, 48);
+    const unsigned long long ab = a > b ? a : b, cd = c > d ? c : d;
+    return ab > cd ? ab : cd;
+}
+
 // Top-k, weights and permutation for T <= 8 tokens in one workgroup of 1024
 // threads.  Expert e of token t carries the key (orderable logit bits, then
 // 255 - e): a larger key is a larger logit, ties going to the lower index, and
-// keys are distinct.  The rank of e is the number of larger keys, counted in
-// four quarters by four threads and summed; ranks below k are the selection,
-// already in order.  Slot s = t*k + j then goes to position offsets[e] + (the
-// number of earlier slots with the same expert).
+// keys are distinct.  For one or two tokens the rank of e is the number of
+// larger keys, counted in four quarters by four threads (all 16 waves busy);
+// ranks below k are the selection, already in order.  For more tokens wave t
+// selects token t's experts: k rounds of a wave-wide maximum over the
+// remaining keys (each lane holds four), the winner leaving the set.  Slot
+// s = t*k + j then goes to position offsets[e] + (the number of earlier slots
+// with the same expert).
 __global__ __launch_bounds__(1024) void k_select_small(const float *__restrict__ logits, int T, int E, int k,
                                                        int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
                                                        int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
                                                        int32_t *__restrict__ active) {
+    constexpr int RANK_T = 2;
     __shared__ float lg[SMALL_T][256];
-    __shared__ __attribute__((aligned(16))) unsigned long long key[SMALL_T][256];
-    __shared__ uint8_t part[4][SMALL_T][256];                              // at most 64 larger keys per quarter
+    __shared__ __attribute__((aligned(16))) unsigned long long key[RANK_T][256];
+    __shared__ uint8_t part[4][RANK_T][256];                               // at most 64 larger keys per quarter
     __shared__ int sel[SMALL_T * 256];
     __shared__ double ex[SMALL_T][256];
     __shared__ int cnt[256];
-    const int tid = threadIdx.x, e = tid & 255, q = tid >> 8;
-    for (int t = q; t < T; t += 4) {
-        const float l = e < E ? logits[t * E + e] : 0.f;
-        lg[t][e] = l;
-        const uint32_t u = __float_as_uint(l + 0.0f);                       // -0 compares equal to +0
-        const uint32_t ord = u ^ ((u >> 31) ? 0xFFFFFFFFu : 0x80000000u);
-        key[t][e] = e < E ? (((unsigned long long)ord << 32) | (uint32_t)(255 - e)) : 0ull;
+    __shared__ uint32_t tmask[256];                                        // bit t: token t selected the expert
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (tid < 256) {
+        cnt[tid] = 0;
+        tmask[tid] = 0u;
     }
-    __syncthreads();
-    for (int t = 0; t < T; ++t) {
-        const unsigned long long me = key[t][e];
-        const ulonglong2 *row = reinterpret_cast<const ulonglong2 *>(&key[t][64 * q]);
-        int r = 0;
-#pragma unroll
-        for (int o2 = 0; o2 < 32; ++o2) {
-            const ulonglong2 u = row[o2];
-            r += (u.x > me ? 1 : 0) + (u.y > me ? 1 : 0);
+    if (T <= RANK_T) {
+        const int e = tid & 255, q = tid >> 8;
+        if (q < T) {
+            const float l = e < E ? logits[q * E + e] : 0.f;
+            lg[q][e] = l;
+            const uint32_t u = __float_as_uint(l + 0.0f);                   // -0 compares equal to +0
+            const uint32_t ord = u ^ ((u >> 31) ? 0xFFFFFFFFu : 0x80000000u);
+            key[q][e] = e < E ? (((unsigned long long)ord << 32) | (uint32_t)(255 - e)) : 0ull;
         }
-        part[q][t][e] = (uint8_t)r;
-    }
-    __syncthreads();
-    for (int t = q; t < T && e < E; t += 4) {
-        const int r = part[0][t][e] + part[1][t][e] + part[2][t][e] + part[3][t][e];
-        if (r < k) sel[t * k + r] = e;
+        __syncthreads();
+        for (int t = 0; t < T; ++t) {
+            const unsigned long long me = key[t][e];
+            const ulonglong2 *row = reinterpret_cast<const ulonglong2 *>(&key[t][64 * q]);
+            int r = 0;
+#pragma unroll
+            for (int o2 = 0; o2 < 32; ++o2) {
+                const ulonglong2 u = row[o2];
+                r += (u.x > me ? 1 : 0) + (u.y > me ? 1 : 0);
+            }
+            part[q][t][e] = (uint8_t)r;
+        }
+        __syncthreads();
+        if (q < T && e < E) {
+            const int r = part[0][q][e] + part[1][q][e] + part[2][q][e] + part[3][q][e];
+            if (r < k) sel[q * k + r] = e;
+        }
+    } else if (wv < T) {
+        unsigned long long kk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            const float l = e < E ? logits[wv * E + e] : 0.f;
+            lg[wv][e] = l;
+            const uint32_t u = __float_as_uint(l + 0.0f);                   // -0 compares equal to +0
+            const uint32_t ord = u ^ ((u >> 31) ? 0xFFFFFFFFu : 0x80000000u);
+            kk[i] = e < E ? (((unsigned long long)ord << 32) | (uint32_t)(255 - e)) : 0ull;
+        }
+        for (int j = 0; j < k; ++j) {
+            const unsigned long long m1 = kk[0] > kk[1] ? kk[0] : kk[1];
+            const unsigned long long m2 = kk[2] > kk[3] ? kk[2] : kk[3];
+            const unsigned long long m = wave_max_u64(m1 > m2 ? m1 : m2);
+            if (lane == 0) sel[wv * k + j] = 255 - (int)(uint32_t)m;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (kk[i] == m) kk[i] = 0ull;                               // keys are distinct: one owner
+        }
     }
     __syncthreads();
     const int S = T * k;
-    // softmax over the selected logits, binary64
+    // softmax over the selected logits, binary64; per-expert slot counts and token sets
     for (int s = tid; s < S; s += 1024) {
-        const int t = s / k;
-        ex[t][s % k] = exp((double)lg[t][sel[s]] - (double)lg[t][sel[t * k]]);
-    }
-    if (tid < E) {
-        int c = 0;
-        for (int s = 0; s < S; ++s) c += sel[s] == tid ? 1 : 0;
-        cnt[tid] = c;
+        const int t = s / k, x = sel[s];
+        ex[t][s % k] = exp((double)lg[t][x] - (double)lg[t][sel[t * k]]);
+        atomicAdd(&cnt[x], 1);
+        atomicOr(&tmask[x], 1u << t);
     }
     __syncthreads();
     for (int s = tid; s < S; s += 1024) {
@@ -342,11 +397,10 @@ __global__ __launch_bounds__(1024) void k_select_small(const float *__restrict__
         }
     }
     __syncthreads();
+    // slot s = t*k + j follows the expert's slots of earlier tokens (a token holds an expert at most once)
     for (int s = tid; s < S; s += 1024) {
-        const int x = sel[s];
-        int before = 0;
-        for (int o = 0; o < s; ++o) before += sel[o] == x ? 1 : 0;
-        perm[cnt[x] + before] = s;
+        const int x = sel[s], t = s / k;
+        perm[cnt[x] + __popc(tmask[x] & ((1u << t) - 1u))] = s;
     }
 }
 

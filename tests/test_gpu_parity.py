@@ -121,7 +121,7 @@ def _check_route(m, x, w_router, E, k, bias=None):
 
 
 ROUTE_CASES = [
-    ("tiny", 4), ("small", 1), ("small", 3), ("small", 8), ("small", 37), ("mid", 6), ("mid", 70), ("decode", 1),
+    ("tiny", 4), ("small", 1), ("small", 2), ("small", 3), ("small", 8), ("small", 37), ("mid", 6), ("mid", 70), ("decode", 1),
     ("decode", 3), ("decode", 5), ("decode", 8), ("decode", 9), ("decode", 64), ("prefill", 512), ("long", 2048), ("long", 2500),
 ]
 
