@@ -744,77 +744,85 @@ __device__ __forceinline__ void routed_gateup_mt(const FfnArgs &a, const int32_t
     }
 }
 
-// Shared gate/up rows for every token of the call, one token at a time against
-// the row's weights held in registers.
-template <int LPR, int CPL, int NR>
-__device__ void shared_gateup_mt(const FfnArgs &a, int row0, float *__restrict__ hs) {
-    constexpr int RPI = 64 / LPR;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int cp = lane % LPR, rsub = lane / LPR;
-    const int H = a.H, Is = a.Is;
-    uint4 gq[NR][CPL], uq[NR][CPL];
+// Shared gate/up rows on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16) for
+// every token of the call: A = the tokens' activations (rows; rows past T are
+// zero), B = 16 weight rows.  Lane 16 g + i supplies the same 8 consecutive K
+// values of A row i and of B column i, so the instruction's own K order inside
+// a step does not matter.  A workgroup takes 16 rows; wave w the K slice
+// [512 w, 512 w + 512) in four quarters of four steps; the slices are summed in
+// LDS and SwiGLU is applied per (token, row).
+typedef __attribute__((ext_vector_type(8))) __bf16 mf_bf16x8_t;
+
+__device__ __forceinline__ mf_acc_t mfma_bf16(uint4 a, uint4 b, mf_acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mf_bf16x8_t, a),
+                                                   __builtin_bit_cast(mf_bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void shared_gateup_mfma(const FfnArgs &a, int row0, float *__restrict__ hs,
+                                                   float *red /* LDS [waves][2][16][16] */) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
+    const int n = lane & 15, g4 = lane >> 4;
+    const int H = a.H, Is = a.Is, T = a.T;
+    const int r = min(row0 + n, Is - 1);
+    const uint16_t *wg = a.sg + (int64_t)r * H, *wu = a.su + (int64_t)r * H;
+    const bool tok = n < T;
+    const uint16_t *xr = static_cast<const uint16_t *>(a.x) + (int64_t)min(n, T - 1) * H;
+    mf_acc_t accg = {}, accu = {};
 #pragma unroll
-    for (int j = 0; j < NR; ++j) {
-        const int r = min(row0 + (wv * NR + j) * RPI + rsub, Is - 1);
+    for (int qt = 0; qt < 4; ++qt) {
+        uint4 bg[4], bu[4], av[4];
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            gq[j][i] = *reinterpret_cast<const uint4 *>(a.sg + (int64_t)r * H + 8 * (cp + LPR * i));
-            uq[j][i] = *reinterpret_cast<const uint4 *>(a.su + (int64_t)r * H + 8 * (cp + LPR * i));
+        for (int st = 0; st < 4; ++st) {
+            const int k = wv * 512 + 128 * qt + 32 * st + 8 * g4;
+            bg[st] = *reinterpret_cast<const uint4 *>(wg + k);
+            bu[st] = *reinterpret_cast<const uint4 *>(wu + k);
+            av[st] = tok ? *reinterpret_cast<const uint4 *>(xr + k) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            accg = mfma_bf16(av[st], bg[st], accg);
+            accu = mfma_bf16(av[st], bu[st], accu);
         }
     }
-#pragma unroll 1
-    for (int t = 0; t < a.T; ++t) {
+    // D: lane (g4, n) holds row row0 + n for tokens 4 g4 .. 4 g4 + 3
 #pragma unroll
-        for (int j = 0; j < NR; ++j)
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                opaque(gq[j][i]);
-                opaque(uq[j][i]);
-            }
-        uint32_t xr[CPL][4];
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + (int64_t)t * H +
-                                                            8 * (cp + LPR * i));
-            xr[i][0] = u.x; xr[i][1] = u.y; xr[i][2] = u.z; xr[i][3] = u.w;
+    for (int j = 0; j < 4; ++j) {
+        const int t = 4 * g4 + j;
+        if (t < T) {
+            red[((wv * 2 + 0) * 16 + t) * 16 + n] = accg[j];
+            red[((wv * 2 + 1) * 16 + t) * 16 + n] = accu[j];
         }
-#pragma unroll
-        for (int j = 0; j < NR; ++j) {
-            float ga = 0.f, ua = 0.f;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const uint32_t g4[4] = {gq[j][i].x, gq[j][i].y, gq[j][i].z, gq[j][i].w};
-                const uint32_t u4[4] = {uq[j][i].x, uq[j][i].y, uq[j][i].z, uq[j][i].w};
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const bf16x2_t xv = __builtin_bit_cast(bf16x2_t, xr[i][v]);
-                    ga = dot2_bf16(__builtin_bit_cast(bf16x2_t, g4[v]), xv, ga);
-                    ua = dot2_bf16(__builtin_bit_cast(bf16x2_t, u4[v]), xv, ua);
-                }
-            }
-            const float g = row_sum<LPR>(ga), u = row_sum<LPR>(ua);
-            const int r = row0 + (wv * NR + j) * RPI + rsub;
-            if (cp == 0 && r < Is) hs[(int64_t)t * Is + r] = silu_mul(g, u);
+    }
+    __syncthreads();
+    for (int i = tid; i < T * 16; i += blockDim.x) {
+        const int t = i >> 4, nn = i & 15, rr = row0 + nn;
+        if (rr >= Is) continue;
+        float g = 0.f, u = 0.f;
+        for (int w = 0; w < nw; ++w) {
+            g += red[((w * 2 + 0) * 16 + t) * 16 + nn];
+            u += red[((w * 2 + 1) * 16 + t) * 16 + nn];
         }
+        hs[(int64_t)t * Is + rr] = silu_mul(g, u);
     }
 }
 
-template <int SLPR, int SCPL>
-__global__ __launch_bounds__(512) void k_gemv_gateup_mt(FfnArgs a, const int32_t *__restrict__ active,
-                                                         int wgs_per_expert, int n_routed_wgs,
+// Shared workgroups first (16 rows each, the longest work items), then the routed ones.  Four waves per SIMD
+// (at most 128 VGPRs) matter more here than the two registers the bound spills.
+__global__ __launch_bounds__(512, 4) void k_gemv_gateup_mt(FfnArgs a, const int32_t *__restrict__ active,
+                                                         int wgs_per_expert, int n_shared_wgs,
                                                          _Float16 *__restrict__ h, float *__restrict__ hs) {
     __shared__ uint32_t cb4[256], sgn[256];
-    __shared__ __attribute__((aligned(16))) uint8_t xq[2][2][MF_MAXH];
+    __shared__ __attribute__((aligned(16))) uint8_t xq[2][2][MF_MAXH];     // shared rows: their slice sums
     __shared__ float xsc[2][MF_MAXH / 32];
     __shared__ float red[(MF_MAXH / MF_KW) * MF_RB * 2 * 2 * 16];
+    static_assert(sizeof(xq) >= (MF_MAXH / MF_KW) * 2 * 16 * 16 * sizeof(float), "shared slice sums");
     const int bid = blockIdx.x;
-    if (bid < n_routed_wgs) {
-        routed_gateup_mt(a, active, bid / wgs_per_expert, (bid % wgs_per_expert) * (16 * MF_RB), h, cb4, sgn, xq,
-                         xsc, red);
+    if (bid < n_shared_wgs) {
+        shared_gateup_mfma(a, bid * 16, hs, reinterpret_cast<float *>(&xq[0][0][0]));
     } else {
-        constexpr int SNR = shared_nr<SCPL>();
-        const int rows = (int)(blockDim.x >> 6) * SNR * (64 / SLPR);
-        shared_gateup_mt<SLPR, SCPL, SNR>(a, (bid - n_routed_wgs) * rows, hs);
+        const int rb = bid - n_shared_wgs;
+        routed_gateup_mt(a, active, rb / wgs_per_expert, (rb % wgs_per_expert) * (16 * MF_RB), h, cb4, sgn, xq, xsc,
+                         red);
     }
 }
 
@@ -1348,18 +1356,12 @@ hipError_t run_down(const FfnArgs &a, int max_active, const _Float16 *h, const f
     return hipGetLastError();
 }
 
-template <int SLPR, int SCPL>
 hipError_t run_gateup_mt(const FfnArgs &a, int max_active, _Float16 *h, float *hs, hipStream_t st) {
-    const int threads = a.H / 8;
+    const int threads = a.H / 8;                                  // H/512 waves, one 512-wide K slice each
     const int wpe = a.I / (16 * MF_RB);
     const int nr = max_active * wpe;
-    int ns = 0;
-    if (a.Is > 0) {
-        const int srows = (threads / 64) * shared_nr<SCPL>() * (64 / SLPR);
-        ns = (a.Is + srows - 1) / srows;
-    }
-    hipLaunchKernelGGL((k_gemv_gateup_mt<SLPR, SCPL>), dim3(nr + ns), dim3(threads), 0, st, a, a.active, wpe, nr, h,
-                       hs);
+    const int ns = (a.Is + 15) / 16;
+    hipLaunchKernelGGL(k_gemv_gateup_mt, dim3(nr + ns), dim3(threads), 0, st, a, a.active, wpe, ns, h, hs);
     return hipGetLastError();
 }
 
@@ -1388,10 +1390,7 @@ hipError_t dispatch_mt(const FfnArgs &a, _Float16 *h, float *hs, hipStream_t st)
     const int max_active = min(a.T * a.k, a.E);
     hipError_t e = hipErrorInvalidValue;
     if (a.stages & STAGE_GATE_UP) {
-        if (a.H == 4096) e = run_gateup_mt<64, 8>(a, max_active, h, hs, st);
-        else if (a.H == 2048) e = run_gateup_mt<64, 4>(a, max_active, h, hs, st);
-        else if (a.H == 1024) e = run_gateup_mt<64, 2>(a, max_active, h, hs, st);
-        else if (a.H == 512) e = run_gateup_mt<64, 1>(a, max_active, h, hs, st);
+        e = run_gateup_mt(a, max_active, h, hs, st);
         if (e != hipSuccess) return e;
     }
     if (!(a.stages & STAGE_DOWN)) return hipSuccess;
