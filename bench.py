@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--prefill-reps", type=int, default=5)
     p.add_argument("--no-q4k", action="store_true", help="skip the 4-bit (q4k) routed-expert workloads")
     p.add_argument("--verify-steps", type=int, default=334, help="steps of the 3-token verify micro-batch")
+    p.add_argument("--no-sweep", action="store_true", help="skip the 2/4/8-token verify micro-batches")
     p.add_argument("--probe", action="store_true",
                    help="hardware-counter probe: --kernel-reps eager launches of the decode gate/up kernel over "
                         "cycled layer copies, then one 1 GiB device-to-device copy (the reference for scaling "
@@ -60,7 +61,7 @@ def parse():
 # WRITE_SIZE counters on that kernel, each scaled by the same counter's reading
 # for a 1 GiB device-to-device copy in the same process.  Valid only for the
 # kernel source it was measured on (sha256 of csrc/ffn_gemv.hip).
-GATEUP_TRAFFIC = {"src_sha256": "406b1b949f99cca6dddd824a68fb2ad461e077dcd713da5b773391b8f3f0b917", "bytes": 68460191}
+GATEUP_TRAFFIC = {"src_sha256": "37644ff49dcf67cf001c6ad248ca9c0753de579ddb2392e91c82578a6c641c71", "bytes": 68459190}
 
 
 def gemv_source_sha():
@@ -218,7 +219,7 @@ def main():
 
     # verifier micro-batches of M = 1 + drafts tokens (independent seeded tokens, same layer copies)
     sweep = {}
-    for M in (2, 4, 8):
+    for M in (() if args.no_sweep else (2, 4, 8)):
         mx = torch.from_numpy(synth.activations("verify", M * vK, H, True, seed=12 + M).view(np.int16)) \
             .view(torch.bfloat16).to(dev)
         mbufs = [LayerBuffers.allocate(layers[0], M) for _ in range(2)]
