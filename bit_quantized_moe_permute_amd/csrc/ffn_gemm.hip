@@ -347,6 +347,7 @@ __device__ __forceinline__ void gu_loop(const FfnArgs &a, int e, int row, int hh
         gu_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w1);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         gu_block<two>(w0, tiles[0], cb4, sgn, n, hh, dprev, acc);
+        __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
         x_store(xs, tiles[1]);
         __syncthreads();
         if (kb + 1 >= nkb) break;
@@ -354,6 +355,7 @@ __device__ __forceinline__ void gu_loop(const FfnArgs &a, int e, int row, int hh
         gu_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w0);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         gu_block<two>(w1, tiles[1], cb4, sgn, n, hh, dprev, acc);
+        __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
         x_store(xs, tiles[0]);
         __syncthreads();
     }
@@ -473,6 +475,7 @@ __device__ __forceinline__ void q4_loop(const uint8_t *W, int64_t NB, int64_t bl
         q4_load(W, NB, bl0 + k1, hh, w1);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         q4_block<two>(w0, tiles[0], hs[0], n, hh, dprev, mprev, acc, accm);
+        __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
         x_store_sums32(xs, tiles[1], hs[1]);
         __syncthreads();
         if (kb + 1 >= nkb) break;
@@ -480,6 +483,7 @@ __device__ __forceinline__ void q4_loop(const uint8_t *W, int64_t NB, int64_t bl
         q4_load(W, NB, bl0 + k2, hh, w0);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         q4_block<two>(w1, tiles[1], hs[1], n, hh, dprev, mprev, acc, accm);
+        __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
         x_store_sums32(xs, tiles[0], hs[0]);
         __syncthreads();
     }
@@ -539,6 +543,7 @@ __device__ __forceinline__ void sg_loop(const FfnArgs &a, int row, int hh, int n
         __builtin_amdgcn_sched_barrier(0);
         sg_stage<two>(b1, tiles[kb & 1], st + 1, n, hh, acc);
         if (!block_start) {                              // end of block kb: publish tile kb + 1
+            __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
             x_store(xs, tiles[(kb + 1) & 1]);
             __syncthreads();
         }
@@ -757,6 +762,7 @@ __device__ __forceinline__ void dn_loop(const FfnArgs &a, int e, int row, int hh
         dn_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w1);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         dn_block<two>(w0, tiles[0], hsum, n, hh, dprev, mprev, acc, accm);
+        __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
         x_store(xs, tiles[1]);
         __syncthreads();
         if (kb + 1 >= nkb) break;
@@ -766,6 +772,7 @@ __device__ __forceinline__ void dn_loop(const FfnArgs &a, int e, int row, int hh
         dn_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w0);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         dn_block<two>(w1, tiles[1], hsum, n, hh, dprev, mprev, acc, accm);
+        __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
         x_store(xs, tiles[0]);
         __syncthreads();
     }
@@ -813,6 +820,7 @@ __device__ __forceinline__ void sd_loop(const FfnArgs &a, int row, int hh, int n
         sd_stage_load(a, row, hh, s1, b1);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         sd_stage<two>(b0, tiles[0], n, hh, acc);
+        __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
         x_store(xs, tiles[1]);
         __syncthreads();
         if (st + 1 >= nst) break;
@@ -820,6 +828,7 @@ __device__ __forceinline__ void sd_loop(const FfnArgs &a, int row, int hh, int n
         sd_stage_load(a, row, hh, s2, b0);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
         sd_stage<two>(b1, tiles[1], n, hh, acc);
+        __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
         x_store(xs, tiles[0]);
         __syncthreads();
     }
