@@ -201,6 +201,16 @@ def main():
     value = K / wall
     log(f"{K} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms -> {value:.0f} tokens/s")
 
+    # the same decode steps on one layer copy (consecutive tokens may find experts in the 256 MB last-level cache)
+    def step1(i):
+        b = bufs[i % 2]
+        forward(layers[0], x[i % n_tok: i % n_tok + 1], b)
+        return b.y
+
+    nwall, _ = graph_steps(step1, K, W)
+    no_cycling = {"tokens_per_s": round(K / nwall, 1), "ms_per_step": round(nwall * 1e3 / K, 5), "layer_copies": 1}
+    log(f"decode on one layer copy (no cycling): {K / nwall:.0f} tokens/s")
+
     # speculative-verify micro-batch: 3 independent tokens per step
     vx_np = synth.activations("verify", 3 * args.verify_steps, H, True)
     vx = torch.from_numpy(vx_np.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -325,7 +335,14 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(L, x_np, args.cpu_seconds)
+        # the GPU layer's outputs for the oracle's sample (one call per token), checked in the same run
+        pb = LayerBuffers.allocate(layers[0], 1)
+        gy, gi = [], []
+        for i in range(200):
+            forward(layers[0], x[i: i + 1], pb)
+            gy.append(pb.y.cpu().numpy()[0].astype(np.float64))
+            gi.append(pb.topk_idx.cpu().numpy()[0].copy())
+        cpu = cpu_baseline(L, x_np, args.cpu_seconds, np.array(gy), np.array(gi))
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -341,6 +358,7 @@ def main():
                  "hbm_frac": round(step_bw / HBM_PEAK_GBS, 4), "graph_gpu_ms": round(gpu_ms, 3)},
         "verify": verify,
         "decode_steer": steer,
+        "decode_no_cycling": no_cycling,
         "decode_q4k": decode_q4k,
         "prefill": prefill,
     }
@@ -467,25 +485,33 @@ def prefill_bench(L, DL, reps, names):
     return out
 
 
-def cpu_baseline(L, x_np, budget_s):
+def cpu_baseline(L, x_np, budget_s, gpu_y, gpu_idx):
     """The oracle (binary64, plain C with OpenMP over rows) on a bounded sample of
-    decode tokens, one call per token, until the time budget is spent."""
+    decode tokens, one call per token, until the time budget is spent.  The GPU
+    layer's outputs for the same tokens (gpu_y, gpu_idx) are checked against the
+    oracle's after the timed loop: routing bit-exact, per-token relative L2."""
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     sp = L.spec
-    done, t0 = 0, time.perf_counter()
+    done, outs, t0 = 0, [], time.perf_counter()
     while True:
         xt = x_np[done: done + 1]
-        oracle.layer(xt, L.w_router, sp.top_k, sp.n_experts, sp.inter, sp.gate_up_fmt, L.gate, L.up, sp.down_fmt,
-                     L.down, L.codebook, bias=L.bias, shared=L.shared)
+        outs.append(oracle.layer(xt, L.w_router, sp.top_k, sp.n_experts, sp.inter, sp.gate_up_fmt, L.gate, L.up,
+                                 sp.down_fmt, L.down, L.codebook, bias=L.bias, shared=L.shared))
         done += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= 200:
+        if el >= budget_s or done >= min(200, len(gpu_y)):
             break
     log(f"oracle: {done} tokens in {el:.1f}s")
+    want = np.concatenate([o["y"] for o in outs])
+    err = np.linalg.norm(gpu_y[:done] - want, axis=1) / np.linalg.norm(want, axis=1)
+    idx_ok = bool(np.array_equal(gpu_idx[:done], np.concatenate([o["topk_idx"] for o in outs])))
+    log(f"parity on the sample: routing exact {idx_ok}, max per-token rel L2 {err.max():.3e}")
     return {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {done} of the 1000 decode tokens, whole layer (route, permute, 8 routed experts, "
-                      f"shared expert, combine) in binary64, {el:.1f} s"}
+                      f"shared expert, combine) in binary64, {el:.1f} s",
+            "parity": {"tokens": done, "routing_exact": idx_ok, "max_rel_l2": float(f"{err.max():.3e}"),
+                       "tolerance": 1e-3}}
 
 
 if __name__ == "__main__":
