@@ -170,11 +170,14 @@ SPECS = {
     "small_mix_b": LayerSpec("small_mix_b", 512, 256, 16, 4, 256, True, 101, FMT_Q4K, FMT_Q2K),
     "mid": LayerSpec("mid", 1024, 512, 32, 8, 512, True, 102, bias_std=0.5),
     "mid_fp32": LayerSpec("mid_fp32", 1024, 512, 32, 8, 0, False, 103),
+    # top-16 routing: the one-ballot slot lookup of the decode kernels covers T*k <= 64 slots
+    "mid_k16": LayerSpec("mid_k16", 1024, 512, 32, 16, 512, True, 104),
 }
 
 # activation seeds per workload
 X_SEEDS = {"tiny": 0, "decode": 11, "verify": 12, "prefill": 13, "long": 14, "long_q4k": 14,
-           "small": 201, "small_q4k": 201, "small_mix_a": 201, "small_mix_b": 201, "mid": 202, "mid_fp32": 203}
+           "small": 201, "small_q4k": 201, "small_mix_a": 201, "small_mix_b": 201, "mid": 202, "mid_fp32": 203,
+           "mid_k16": 204}
 BIAS_SEEDS = {"prefill": 23, "mid": 24}
 TOKENS = {"tiny": 4, "decode": 1000, "verify": 3 * 334, "prefill": 512, "long": 11709, "long_q4k": 11709}
 

@@ -235,8 +235,10 @@ LAYER_CASES = [
     ("small_q4k", 1, 0), ("small_q4k", 3, 0), ("small_q4k", 4, 0), ("small_q4k", 3, 1), ("small_q4k", 37, 0),
     ("small_q4k", 3, 3), ("small_q4k", 70, 0),
     ("small_mix_a", 2, 0), ("small_mix_a", 37, 0), ("small_mix_b", 2, 0), ("small_mix_b", 37, 0),
-    # one token with a q2k down (matrix-core down) on each down shape
+    # one token on each down shape
     ("mid", 1, 0), ("small_mix_b", 1, 0), ("mid", 1, 2),
+    # top-16: 16, 32 and 64 slots on the decode kernels, 80 slots on the grouped GEMM
+    ("mid_k16", 1, 0), ("mid_k16", 2, 0), ("mid_k16", 4, 0), ("mid_k16", 5, 0),
 ]
 
 
