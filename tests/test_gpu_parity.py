@@ -419,3 +419,43 @@ def test_layer_with_steering_matches_oracle(m, name, T):
     forward(DL, dev_x(x), b2)
     torch.cuda.synchronize()
     assert torch.equal(b.slot_out, b2.slot_out)
+
+
+# ----------------------------------------------------------------------------
+# HIP graph capture of the whole layer
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name,T,steer", [("mid", 1, False), ("mid", 3, True), ("mid", 8, False),
+                                          ("mid", 37, True)])
+def test_layer_graph_replay_matches_eager(m, name, T, steer):
+    """route -> expert FFN -> combine captured once in a HIP graph and replayed on new inputs (copied into the
+    captured input buffer between replays, with eager work and synchronizations in between): every replay equals
+    an eager run on the same input bit for bit."""
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward
+    note(f"graph replay {name} T={T} steer={steer}")
+    L = _layer(name)
+    sp = L.spec
+    DL = DeviceLayer.from_synth(L)
+    if steer:
+        DL.set_steering(synth.steer_direction(sp.hidden), 1.0)
+    xs = [dev_x(synth.activations(name, T, sp.hidden, sp.x_bf16, seed=600 + r)) for r in range(3)]
+    xin = torch.empty_like(xs[0])
+    xin.copy_(xs[0])
+    bg, be = LayerBuffers.allocate(DL, T), LayerBuffers.allocate(DL, T)
+    forward(DL, xin, bg)                                       # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            forward(DL, xin, bg)
+    torch.cuda.synchronize()
+    for r in range(3):
+        xin.copy_(xs[r])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        forward(DL, xs[r], be)
+        torch.cuda.synchronize()
+        assert torch.equal(bg.topk_idx, be.topk_idx)
+        assert torch.equal(bg.y, be.y), f"replay {r}"
