@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--no-q4k", action="store_true", help="skip the 4-bit (q4k) routed-expert workloads")
     p.add_argument("--verify-steps", type=int, default=334, help="steps of the 3-token verify micro-batch")
     p.add_argument("--no-sweep", action="store_true", help="skip the 2/4/8-token verify micro-batches")
+    p.add_argument("--probe-gemm", action="store_true",
+                   help="hardware-counter probe: --kernel-reps eager launches of the prefill gate/up grouped GEMM "
+                        "on the first 2048-token chunk of the long prompt")
     p.add_argument("--probe", action="store_true",
                    help="hardware-counter probe: --kernel-reps eager launches of the decode gate/up kernel over "
                         "cycled layer copies, then one 1 GiB device-to-device copy (the reference for scaling "
@@ -101,6 +104,28 @@ def probe(args):
     torch.cuda.synchronize()
     print(json.dumps({"probe": "decode gate/up", "launches": reps, "copy_bytes": 1 << 30,
                       "gemv_src_sha256": gemv_source_sha()}), flush=True)
+
+
+def probe_gemm(args):
+    """Eager launches of the prefill gate/up grouped GEMM (first 2048-token chunk of the long prompt, one layer
+    copy), for counter collection (no timing)."""
+    import torch
+
+    import synth
+    from bit_quantized_moe_permute_amd import moe_expert_gate_up, moe_route
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers
+
+    L = synth.make_layer(synth.SPECS["decode"])
+    DL = DeviceLayer.from_synth(L)
+    T = 2048
+    x = torch.from_numpy(synth.activations("long", T, L.spec.hidden, True).view(np.int16)).view(torch.bfloat16).cuda()
+    b = LayerBuffers.allocate(DL, T)
+    moe_route(x, DL.w_router, DL.E, DL.k, b.topk_idx, b.topk_w, b.offsets, b.perm, b.active, b.ws_route)
+    reps = args.kernel_reps or 10
+    for _ in range(reps):
+        moe_expert_gate_up(DL.desc, x, b.topk_idx, b.offsets, b.perm, b.active, b.ws_ffn)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "prefill gate/up grouped GEMM", "tokens": T, "launches": reps}), flush=True)
 
 
 def graph_steps(step, K, W):
@@ -162,6 +187,9 @@ def main():
 
     if args.probe:
         probe(args)
+        return
+    if args.probe_gemm:
+        probe_gemm(args)
         return
 
     import torch
