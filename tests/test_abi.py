@@ -144,3 +144,20 @@ def test_prepare_and_combine_reject_bad_arguments(lib):
     assert h(p, p, None, 1, 8, 4096, p, float("nan"), p, None) == 1           # strength not finite
     assert "finite" in _err(lib)
     assert h(p, p, None, 1, 8, 4096, p, float("inf"), p, None) == 1
+
+
+def test_plain_c_consumer(tmp_path):
+    """tests/abi_consumer.c: a C program that includes moe2bit.h and links the library (gcc, no GPU)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    exe = tmp_path / "abi_consumer"
+    libdir = os.path.dirname(LIB)
+    cmd = [gcc, "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "abi_consumer.c"), "-L", libdir, "-lmoe2bit", f"-Wl,-rpath,{libdir}",
+           "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0 and out.stdout.strip().endswith("ok"), out.stdout + out.stderr
