@@ -459,3 +459,43 @@ def test_layer_graph_replay_matches_eager(m, name, T, steer):
         torch.cuda.synchronize()
         assert torch.equal(bg.topk_idx, be.topk_idx)
         assert torch.equal(bg.y, be.y), f"replay {r}"
+
+
+# ----------------------------------------------------------------------------
+# degenerate blocks: zero scales
+# ----------------------------------------------------------------------------
+def _zero_scales(blocks: np.ndarray, fmt: int, frac: float, seed: int) -> np.ndarray:
+    """A copy of canonical blocks with the fp16 scale d (and dmin for q2k/q4k) of a random fraction of blocks
+    set to +0: such blocks decode to zeros, and the grouped GEMM must keep its running block scale across them."""
+    bb = oracle.BLOCK_BYTES[fmt]
+    b = blocks.copy().reshape(-1, bb)
+    pick = np.random.default_rng(seed).random(b.shape[0]) < frac
+    b[pick, 0:2] = 0
+    if fmt != oracle.FMT_IQ2X:
+        b[pick, 2:4] = 0
+    return b.reshape(-1)
+
+
+@pytest.mark.parametrize("name,T,path", [("small", 1, 0), ("small", 3, 0), ("small", 6, 0), ("small", 37, 0),
+                                         ("small", 3, 3), ("small", 2, 1), ("small_q4k", 1, 0), ("small_q4k", 37, 0)])
+def test_layer_with_zero_scale_blocks(m, name, T, path):
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward
+    note(f"zero-scale blocks {name} T={T} path={path}")
+    L = _layer(name)
+    sp = L.spec
+    gate = _zero_scales(L.gate, sp.gate_up_fmt, 0.2, 1)
+    up = _zero_scales(L.up, sp.gate_up_fmt, 0.2, 2)
+    down = _zero_scales(L.down, sp.down_fmt, 0.2, 3)
+    DL = DeviceLayer(sp.hidden, sp.inter, sp.n_experts, sp.top_k, sp.gate_up_fmt, sp.down_fmt, gate, up, down,
+                     L.codebook, L.w_router, L.bias, L.shared, path=path)
+    x = synth.activations(name, T, sp.hidden, sp.x_bf16, seed=950 + T)
+    b = LayerBuffers.allocate(DL, T)
+    forward(DL, dev_x(x), b)
+    torch.cuda.synchronize()
+    ref = oracle.layer(x, L.w_router, sp.top_k, sp.n_experts, sp.inter, sp.gate_up_fmt, gate, up, sp.down_fmt, down,
+                       L.codebook, bias=L.bias, shared=L.shared)
+    assert np.array_equal(b.topk_idx.cpu().numpy(), ref["topk_idx"])
+    assert rel_l2_rows(b.slot_out.cpu().numpy(), ref["slot_out"]).max() <= TOL
+    err = rel_l2_rows(b.y.cpu().numpy(), ref["y"])
+    note(f"  max per-token rel L2 = {err.max():.3e}")
+    assert err.max() <= TOL
