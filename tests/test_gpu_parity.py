@@ -499,3 +499,27 @@ def test_layer_with_zero_scale_blocks(m, name, T, path):
     err = rel_l2_rows(b.y.cpu().numpy(), ref["y"])
     note(f"  max per-token rel L2 = {err.max():.3e}")
     assert err.max() <= TOL
+
+
+# ----------------------------------------------------------------------------
+# activation range: the per-group scaling of the e4m3 pieces and the fp16 tiles
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("scale_exp", [-6, -3, 3, 6])
+@pytest.mark.parametrize("T", [1, 3, 37])
+def test_layer_activation_scales(m, scale_exp, T):
+    """x scaled by powers of two from 2^-6 to 2^6 (exact in bf16): routing, slot and layer outputs still match the
+    oracle on the decode, verify and grouped-GEMM kernels.  This is the edge of the supported range: the routed
+    SwiGLU output h is carried in fp16 and grows as |x|^2, so at 2^8 it overflows and at 2^-10 it falls into
+    fp16's subnormals (the numerics comment of moe_expert_ffn states the range)."""
+    note(f"activation scale 2^{scale_exp} T={T}")
+    L = _layer("small")
+    sp = L.spec
+    x = synth.to_bf16_bits(synth.bf16_bits_to_f32(synth.activations("small", T, sp.hidden, True, seed=970 + T))
+                           * np.float32(2.0 ** scale_exp))
+    got = _run_layer(m, L, x, 0)
+    ref = _oracle_layer(L, x)
+    assert np.array_equal(got["topk_idx"], ref["topk_idx"])
+    assert rel_l2_rows(got["slot_out"], ref["slot_out"]).max() <= TOL
+    err = rel_l2_rows(got["y"], ref["y"])
+    note(f"  max per-token rel L2 = {err.max():.3e}")
+    assert err.max() <= TOL
