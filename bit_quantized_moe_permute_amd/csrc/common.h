@@ -182,4 +182,48 @@ __device__ __forceinline__ void q4k_sub8(const uint8_t *prep, int64_t NB, int64_
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
+// Power-of-two exponent s of a token's routed SwiGLU output h, from the largest magnitude of its activations:
+// h grows as |x|^2, so the fp16 copy of h carries h * 2^-s, which stays near unit scale whatever the input range
+// (s = 0 for a largest |x| in [2, 4)); the down projection multiplies its sums by 2^s.  Every kernel derives s
+// from the same bf16 x row, so all of them agree.
+__device__ __forceinline__ int h_sigma(float max_abs_x) {
+    if (!(max_abs_x > 0.f)) return 0;
+    return min(max(2 * (ilogbf(max_abs_x) - 1), -100), 100);
+}
+
+// Wave-wide maximum of a non-negative float, the same in every lane: within each row of 16 lanes by DPP (quad
+// swaps 1 and 2, half-row mirror, row mirror), then across the four rows from one lane of each.
+template <int CTRL> __device__ __forceinline__ float fmax_dpp(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF,
+                                                               false)));
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+    v = fmax_dpp<0xB1>(v);
+    v = fmax_dpp<0x4E>(v);
+    v = fmax_dpp<0x141>(v);
+    v = fmax_dpp<0x140>(v);
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// largest magnitude of the two bf16 values in a word
+__device__ __forceinline__ float bf16x2_absmax(uint32_t w) {
+    return fmaxf(fabsf(__uint_as_float(w << 16)), fabsf(__uint_as_float(w & 0xFFFF0000u)));
+}
+
+// Running largest magnitude over bf16 pairs, kept as two 16-bit fields: with the sign bits cleared, bf16 bit
+// patterns order as the magnitudes they encode, so one packed 16-bit integer maximum per word does the update.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_absmax_acc(uint32_t acc, uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, acc),
+                                                                  __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu)));
+}
+// the larger of the two fields, as a float
+__device__ __forceinline__ float bf16x2_absmax_value(uint32_t acc) {
+    return __uint_as_float(max(acc << 16, acc & 0xFFFF0000u));
+}
+
 }  // namespace moe

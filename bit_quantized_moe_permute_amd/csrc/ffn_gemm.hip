@@ -562,6 +562,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
     __shared__ uint32_t cb4[256], sgn[128];
     __shared__ const uint16_t *src[TOK];
     __shared__ int dst[TOK];
+    __shared__ float hfac[TOK];                                 // routed rows: 2^-sigma of the row's token
     __shared__ uint4 tiles[2][TOK * 32];
     __shared__ __attribute__((aligned(16))) _Float16 hsum[2][TOK][16];
     Item it;
@@ -576,8 +577,13 @@ __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
     if (tid < TOK) {
         const int m = tid < it.n ? tid : 0;                  // rows past the tile alias row 0
         const uint16_t *s;
-        if (!it.shared) s = reinterpret_cast<const uint16_t *>(g.x16) + (int64_t)(a.perm[it.p0 + m] / a.k) * H;
-        else s = static_cast<const uint16_t *>(a.x) + (int64_t)(it.p0 + m) * H;
+        if (!it.shared) {
+            const int tok = a.perm[it.p0 + m] / a.k;
+            s = reinterpret_cast<const uint16_t *>(g.x16) + (int64_t)tok * H;
+            hfac[tid] = ldexpf(1.f, -a.hsig[tok]);
+        } else {
+            s = static_cast<const uint16_t *>(a.x) + (int64_t)(it.p0 + m) * H;
+        }
         src[tid] = s;
         dst[tid] = tid < it.n ? it.p0 + tid : -1;
     }
@@ -615,8 +621,9 @@ __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
                 for (int v = 0; v < 16; ++v) {
                     const int tt = 32 * tf + drow(v, lane), d = dst[tt];
                     if (d >= 0)
-                        g.h[(int64_t)d * a.I + r4] = (_Float16)silu_mul(accq[tf][v] * dprev - accm[tf][v] * mprev,
-                                                                        xch[((wv & 3) * TOK + tt) * 32 + n]);
+                        g.h[(int64_t)d * a.I + r4] = (_Float16)(silu_mul(accq[tf][v] * dprev - accm[tf][v] * mprev,
+                                                                         xch[((wv & 3) * TOK + tt) * 32 + n]) *
+                                                                hfac[tt]);
                 }
         }
     } else if (!it.shared) {
@@ -628,10 +635,10 @@ __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
         for (int tf = 0; tf < 2; ++tf)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int d = dst[32 * tf + drow(v, lane)];
+                const int tt = 32 * tf + drow(v, lane), d = dst[tt];
                 if (d >= 0)
                     g.h[(int64_t)d * a.I + row] =
-                        (_Float16)silu_mul(acc[tf][0][v] * dprev[0], acc[tf][1][v] * dprev[1]);
+                        (_Float16)(silu_mul(acc[tf][0][v] * dprev[0], acc[tf][1][v] * dprev[1]) * hfac[tt]);
             }
     } else {
         if (two) sg_loop<true>(a, row, hh, n, src, tiles, acc);
@@ -842,6 +849,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
     __shared__ const uint16_t *src[TOK];
     __shared__ const uint16_t *src_lo[TOK];
     __shared__ int dst[TOK];
+    __shared__ float hfac[TOK];                                 // routed rows: 2^sigma of the row's token
     __shared__ uint4 tiles[2][TOK * 32];
     __shared__ __attribute__((aligned(16))) _Float16 hsum[2][TOK][16];
     Item it;
@@ -855,6 +863,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
             src[tid] = reinterpret_cast<const uint16_t *>(g.h) + (int64_t)(it.p0 + m) * I;
             src_lo[tid] = nullptr;
             dst[tid] = tid < it.n ? a.perm[it.p0 + tid] : -1;          // output slot
+            hfac[tid] = ldexpf(1.f, a.hsig[a.perm[it.p0 + m] / a.k]);
         } else {
             src[tid] = g.hs_hi + (int64_t)(it.p0 + m) * a.Is;
             src_lo[tid] = g.hs_lo + (int64_t)(it.p0 + m) * a.Is;
@@ -881,8 +890,8 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
         for (int tf = 0; tf < 2; ++tf)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int d = dst[32 * tf + drow(v, lane)];
-                if (d >= 0) a.slot_out[(int64_t)d * H + row] = acc[tf][v] * dprev - accm[tf][v] * mprev;
+                const int tt = 32 * tf + drow(v, lane), d = dst[tt];
+                if (d >= 0) a.slot_out[(int64_t)d * H + row] = (acc[tf][v] * dprev - accm[tf][v] * mprev) * hfac[tt];
             }
     } else {
         if (two) sd_loop<true>(a, row, hh, n, src, src_lo, tiles, acc);
@@ -897,26 +906,37 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
     }
 }
 
-// x (bf16) -> fp16 copy, 8 elements per thread
-__global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t *__restrict__ x, _Float16 *__restrict__ y,
-                                                  int64_t n8) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const uint4 v = reinterpret_cast<const uint4 *>(x)[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    f16x8_t o;
+// x (bf16) -> fp16 copy, one workgroup per token row, 8 elements per thread and step; also the exponent of
+// the token's routed h scale (from the row's largest |x|) into hsig[token]
+__global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t *__restrict__ x, _Float16 *__restrict__ y, int H,
+                                                  int32_t *__restrict__ hsig) {
+    __shared__ float wmax[4];
+    const int t = blockIdx.x, n8 = H / 8;
+    const uint4 *xr = reinterpret_cast<const uint4 *>(x + (int64_t)t * H);
+    f16x8_t *yr = reinterpret_cast<f16x8_t *>(y + (int64_t)t * H);
+    float mx = 0.f;
+    for (int i = threadIdx.x; i < n8; i += 256) {
+        const uint4 v = xr[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        f16x8_t o;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        o[2 * j] = (_Float16)__uint_as_float(w[j] << 16);
-        o[2 * j + 1] = (_Float16)__uint_as_float(w[j] & 0xFFFF0000u);
+        for (int j = 0; j < 4; ++j) {
+            o[2 * j] = (_Float16)__uint_as_float(w[j] << 16);
+            o[2 * j + 1] = (_Float16)__uint_as_float(w[j] & 0xFFFF0000u);
+            mx = fmaxf(mx, bf16x2_absmax(w[j]));
+        }
+        yr[i] = o;
     }
-    reinterpret_cast<f16x8_t *>(y)[i] = o;
+    mx = wave_max_f32(mx);
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) hsig[t] = h_sigma(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
 }
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 struct Layout {
-    size_t x16, h, hs_hi, hs_lo, total;
+    size_t x16, h, hs_hi, hs_lo, hsig, total;
 };
 Layout layout(int H, int I, int k, int Is, int T) {
     Layout L;
@@ -924,7 +944,8 @@ Layout layout(int H, int I, int k, int Is, int T) {
     L.h = L.x16 + align256((size_t)T * H * 2);
     L.hs_hi = L.h + align256((size_t)T * k * I * 2);
     L.hs_lo = L.hs_hi + align256((size_t)T * Is * 2);
-    L.total = L.hs_lo + align256((size_t)T * Is * 2);
+    L.hsig = L.hs_lo + align256((size_t)T * Is * 2);
+    L.total = L.hsig + align256((size_t)T * 4);
     return L;
 }
 
@@ -955,14 +976,14 @@ hipError_t launch_ffn_gemm(const FfnArgs &a, hipStream_t st) {
     g.h = reinterpret_cast<_Float16 *>(ws + L.h);
     g.hs_hi = reinterpret_cast<uint16_t *>(ws + L.hs_hi);
     g.hs_lo = reinterpret_cast<uint16_t *>(ws + L.hs_lo);
+    g.a.hsig = reinterpret_cast<int32_t *>(ws + L.hsig);
     const int S = a.T * a.k;
     const int max_tiles = (S + TOK - 1) / TOK + (S < a.E ? S : a.E);   // sum_e ceil(n_e / TOK) bound
     const int st_tiles = (a.T + TOK - 1) / TOK;
     hipError_t e = hipSuccess;
     if (a.stages & STAGE_GATE_UP) {
-        const int64_t n8 = (int64_t)a.T * a.H / 8;
-        hipLaunchKernelGGL(k_x_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
-                           static_cast<const uint16_t *>(a.x), const_cast<_Float16 *>(g.x16), n8);
+        hipLaunchKernelGGL(k_x_to_f16, dim3(a.T), dim3(256), 0, st, static_cast<const uint16_t *>(a.x),
+                           const_cast<_Float16 *>(g.x16), a.H, g.a.hsig);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int rpi = a.fmt_gu == FMT_Q4K ? ROWS / 2 : ROWS;
         const int G = max_tiles * (a.I / rpi) + (a.Is > 0 ? st_tiles * (a.Is / ROWS) : 0);

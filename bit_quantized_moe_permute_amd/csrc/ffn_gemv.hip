@@ -138,6 +138,22 @@ __device__ void routed_gateup(const FfnArgs &a, int e, const Tokens<MAXM> &tk, i
             ud[j][i] = Ud[bl];
         }
     }
+    // h scale exponent per token: the largest |x| over the row (the LPR lanes of a row cover it), after the
+    // weight requests
+    int sig[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        uint32_t mx = 0u;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+#pragma unroll
+            for (int v = 0; v < 32; ++v) mx = bf16x2_absmax_acc(mx, xr[i][m][v]);
+        sig[m] = h_sigma(wave_max_f32(bf16x2_absmax_value(mx)));  // the lanes of a wave cover the whole row
+    }
+    if (row0 == 0 && wv == 0 && lane == 0)
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m)
+            if (m < tk.n) a.hsig[tk.tok[m]] = sig[m];
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
         float ga[MAXM], ua[MAXM];
@@ -152,7 +168,7 @@ __device__ void routed_gateup(const FfnArgs &a, int e, const Tokens<MAXM> &tk, i
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) {
             const float g = row_sum<LPR>(ga[m]), u = row_sum<LPR>(ua[m]);
-            if (m < tk.n && cp == 0 && r < I) h[(int64_t)tk.slot[m] * I + r] = (_Float16)silu_mul(g, u);
+            if (m < tk.n && cp == 0 && r < I) h[(int64_t)tk.slot[m] * I + r] = (_Float16)ldexpf(silu_mul(g, u), -sig[m]);
         }
     }
 }
@@ -195,6 +211,9 @@ __device__ void routed_gateup_q4k(const FfnArgs &a, int e, const Tokens<MAXM> &t
     const int64_t nb_row = H / MOE_QK, nb_mat = (int64_t)I * nb_row, NB = nb_mat * a.E;
     uint32_t xr[CPL][MAXM][16];
     float xs[CPL][MAXM];
+    uint32_t xmax[MAXM];                                      // largest |x| of the lane's chunks, two bf16 fields
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) xmax[m] = 0u;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int ch = cp + LPR * i;
@@ -211,6 +230,7 @@ __device__ void routed_gateup_q4k(const FfnArgs &a, int e, const Tokens<MAXM> &t
                 for (int k = 0; k < 4; ++k) {
                     xr[i][m][4 * v + k] = w4[k];
                     sum += __uint_as_float(w4[k] << 16) + __uint_as_float(w4[k] & 0xFFFF0000u);
+                    xmax[m] = bf16x2_absmax_acc(xmax[m], w4[k]);
                 }
             }
             xs[i][m] = sum;
@@ -230,6 +250,11 @@ __device__ void routed_gateup_q4k(const FfnArgs &a, int e, const Tokens<MAXM> &t
             um[jr][i] = *reinterpret_cast<const uint4 *>(a.up + NB * 128 + bl * 16);
         }
     }
+    int sig[MAXM];                                            // h scale exponent per token (largest |x| of the row)
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        sig[m] = h_sigma(wave_max_f32(bf16x2_absmax_value(xmax[m])));  // the lanes of a wave cover the whole row
+    }
 #pragma unroll
     for (int jr = 0; jr < NR; ++jr) {
         float ga[MAXM], ua[MAXM];
@@ -245,9 +270,13 @@ __device__ void routed_gateup_q4k(const FfnArgs &a, int e, const Tokens<MAXM> &t
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) {
             const float g = row_sum<LPR>(ga[m]), u = row_sum<LPR>(ua[m]);
-            if (m < tk.n && cp == 0 && r < I) h[(int64_t)tk.slot[m] * I + r] = (_Float16)silu_mul(g, u);
+            if (m < tk.n && cp == 0 && r < I) h[(int64_t)tk.slot[m] * I + r] = (_Float16)ldexpf(silu_mul(g, u), -sig[m]);
         }
     }
+    if (row0 == 0 && wv == 0 && lane == 0)
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m)
+            if (m < tk.n) a.hsig[tk.tok[m]] = sig[m];
 }
 
 // Shared gate/up (bf16 rows of H = 8*LPR*CPL).
@@ -376,7 +405,7 @@ __device__ __forceinline__ mf_acc_t mfma_f8f4(const mf_ab_t &a, uint4 b) {
 // Activation pieces of one token: thread tid converts x[8 tid .. 8 tid + 7]
 // (bf16 pairs in xv) into e4m3 hi and lo pieces at xhi/xlo[8 tid ..]; the four
 // threads of a 32-value group share the scale 2^-s, stored at xsc[tid / 4].
-__device__ __forceinline__ void x_to_pieces(uint4 xv, int tid, uint8_t *xhi, uint8_t *xlo, float *xsc) {
+__device__ __forceinline__ float x_to_pieces(uint4 xv, int tid, uint8_t *xhi, uint8_t *xlo, float *xsc) {
     const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
     float mx = 0.f;
 #pragma unroll
@@ -400,6 +429,19 @@ __device__ __forceinline__ void x_to_pieces(uint4 xv, int tid, uint8_t *xhi, uin
     }
     *reinterpret_cast<uint2 *>(xhi + 8 * tid) = make_uint2(hi2[0], hi2[1]);
     *reinterpret_cast<uint2 *>(xlo + 8 * tid) = make_uint2(lo2[0], lo2[1]);
+    return mx;                                                // the group's largest |x|
+}
+
+// Largest |x| of a token over the workgroup: each wave's maximum into xmx[wave]; read back after a barrier.
+__device__ __forceinline__ void wave_max_to(float mx, float *xmx) {
+    mx = wave_max_f32(mx);
+    if ((threadIdx.x & 63) == 0) xmx[threadIdx.x >> 6] = mx;
+}
+
+__device__ __forceinline__ int sigma_from(const float *xmx, int nw) {
+    float mx = 0.f;
+    for (int w = 0; w < nw; ++w) mx = fmaxf(mx, xmx[w]);
+    return h_sigma(mx);
 }
 
 // active: the active-expert list, read-only here; with uniform indices it is
@@ -410,7 +452,8 @@ template <int MAXM>
 __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32_t *__restrict__ active, int ai,
                                                    int row0,
                                                    _Float16 *__restrict__ h, uint32_t *cb4, uint32_t *sgn,
-                                                   uint8_t (*xq)[2][MF_MAXH], float (*xsc)[MF_MAXH / 32], float *red) {
+                                                   uint8_t (*xq)[2][MF_MAXH], float (*xsc)[MF_MAXH / 32], float *red,
+                                                   float (*xmx)[MF_MAXH / MF_KW]) {
     constexpr int NP = (MAXM + 1) / 2;                       // products per K step (two tokens each)
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
     const int n = lane & 15, qd = lane >> 4;
@@ -463,7 +506,7 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
             if ((tid & 3) == 0) xsc[m][tid >> 2] = 0.f;
             continue;
         }
-        x_to_pieces(xv[m], tid, xq[m][0], xq[m][1], xsc[m]);
+        wave_max_to(x_to_pieces(xv[m], tid, xq[m][0], xq[m][1], xsc[m]), xmx[m]);
     }
     if (ai >= n_active) return;                               // whole workgroup: fewer experts than launched
     // --- every token of the call is multiplied (the products hold MAXM
@@ -566,8 +609,9 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
             g += red[(((w * MF_RB + rb) * 2 + 0) * MAXM + m) * 16 + nn];
             u += red[(((w * MF_RB + rb) * 2 + 1) * MAXM + m) * 16 + nn];
         }
-        h[(int64_t)sl * I + r] = (_Float16)silu_mul(g, u);
+        h[(int64_t)sl * I + r] = (_Float16)ldexpf(silu_mul(g, u), -sigma_from(xmx[m], nw));
     }
+    if (row0 == 0 && tid < nt) a.hsig[tid] = sigma_from(xmx[tid], nw);
 }
 
 // ---------------------------------------------------------------------------
@@ -590,7 +634,7 @@ constexpr int MT_MAX = 8;
 __device__ __forceinline__ void routed_gateup_mt(const FfnArgs &a, const int32_t *__restrict__ active, int ai,
                                                  int row0, _Float16 *__restrict__ h, uint32_t *cb4, uint32_t *sgn,
                                                  uint8_t (*xq)[2][MF_MAXH], float (*xsc)[MF_MAXH / 32],
-                                                 float *red) {
+                                                 float *red, float (*xmx)[MF_MAXH / MF_KW]) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
     const int n = lane & 15, qd = lane >> 4;
     const int H = a.H, I = a.I;
@@ -638,8 +682,8 @@ __device__ __forceinline__ void routed_gateup_mt(const FfnArgs &a, const int32_t
         if (row < 256) sgn[row] = sign_spread(row & 0x7F);
     }
     if (ai >= n_active) return;                               // whole workgroup
-    x_to_pieces(xv0, tid, xq[0][0], xq[0][1], xsc[0]);
-    if (s1 >= 0) x_to_pieces(xv1, tid, xq[1][0], xq[1][1], xsc[1]);
+    wave_max_to(x_to_pieces(xv0, tid, xq[0][0], xq[0][1], xsc[0]), xmx[0]);
+    if (s1 >= 0) wave_max_to(x_to_pieces(xv1, tid, xq[1][0], xq[1][1], xsc[1]), xmx[1]);
     else if ((tid & 3) == 0) xsc[1][tid >> 2] = 0.f;
     const int qa = n >> 2, at = (n >> 1) & 1, ap = n & 1;
     const bool arow = (qd >> 1) == (qa & 1);
@@ -659,10 +703,10 @@ __device__ __forceinline__ void routed_gateup_mt(const FfnArgs &a, const int32_t
         // first pass's were made above, while the weights streamed in)
         if (!first) {
             const uint4 v0 = *reinterpret_cast<const uint4 *>(xb + (int64_t)(s0 / a.k) * H + 8 * tid);
-            x_to_pieces(v0, tid, xq[0][0], xq[0][1], xsc[0]);
+            wave_max_to(x_to_pieces(v0, tid, xq[0][0], xq[0][1], xsc[0]), xmx[0]);
             if (s1 >= 0) {
                 const uint4 v1 = *reinterpret_cast<const uint4 *>(xb + (int64_t)(s1 / a.k) * H + 8 * tid);
-                x_to_pieces(v1, tid, xq[1][0], xq[1][1], xsc[1]);
+                wave_max_to(x_to_pieces(v1, tid, xq[1][0], xq[1][1], xsc[1]), xmx[1]);
             } else if ((tid & 3) == 0) {
                 xsc[1][tid >> 2] = 0.f;
             }
@@ -738,8 +782,9 @@ __device__ __forceinline__ void routed_gateup_mt(const FfnArgs &a, const int32_t
                 g += red[(((w * MF_RB + rb) * 2 + 0) * 2 + m) * 16 + nn];
                 u += red[(((w * MF_RB + rb) * 2 + 1) * 2 + m) * 16 + nn];
             }
-            h[(int64_t)sl * I + r] = (_Float16)silu_mul(g, u);
+            h[(int64_t)sl * I + r] = (_Float16)ldexpf(silu_mul(g, u), -sigma_from(xmx[m], nw));
         }
+        if (row0 == 0 && tid < 2 && (tid == 0 || s1 >= 0)) a.hsig[(tid ? s1 : s0) / a.k] = sigma_from(xmx[tid], nw);
         __syncthreads();                                       // LDS pieces and sums are reused by the next pass
     }
 }
@@ -815,6 +860,7 @@ __global__ __launch_bounds__(512, 4) void k_gemv_gateup_mt(FfnArgs a, const int3
     __shared__ __attribute__((aligned(16))) uint8_t xq[2][2][MF_MAXH];     // shared rows: their slice sums
     __shared__ float xsc[2][MF_MAXH / 32];
     __shared__ float red[(MF_MAXH / MF_KW) * MF_RB * 2 * 2 * 16];
+    __shared__ float xmx[2][MF_MAXH / MF_KW];
     static_assert(sizeof(xq) >= (MF_MAXH / MF_KW) * 2 * 16 * 16 * sizeof(float), "shared slice sums");
     const int bid = blockIdx.x;
     if (bid < n_shared_wgs) {
@@ -822,7 +868,7 @@ __global__ __launch_bounds__(512, 4) void k_gemv_gateup_mt(FfnArgs a, const int3
     } else {
         const int rb = bid - n_shared_wgs;
         routed_gateup_mt(a, active, rb / wgs_per_expert, (rb % wgs_per_expert) * (16 * MF_RB), h, cb4, sgn, xq, xsc,
-                         red);
+                         red, xmx);
     }
 }
 
@@ -835,10 +881,12 @@ __global__ __launch_bounds__(512) void k_gemv_gateup_mfma(FfnArgs a, const int32
     __shared__ __attribute__((aligned(16))) uint8_t xq[MAXM][2][MF_MAXH];
     __shared__ float xsc[MAXM][MF_MAXH / 32];
     __shared__ float red[(MF_MAXH / MF_KW) * MF_RB * 2 * MAXM * 16];
+    __shared__ float xmx[MAXM][MF_MAXH / MF_KW];
     const int bid = blockIdx.x;
     if (bid < n_routed_wgs) {
         const int ai = bid / wgs_per_expert;
-        routed_gateup_mfma<MAXM>(a, active, ai, (bid % wgs_per_expert) * (16 * MF_RB), h, cb4, sgn, xq, xsc, red);
+        routed_gateup_mfma<MAXM>(a, active, ai, (bid % wgs_per_expert) * (16 * MF_RB), h, cb4, sgn, xq, xsc, red,
+                                 xmx);
     } else {
         Tokens<MAXM> tk;
         all_tokens<MAXM>(a, tk);
@@ -946,6 +994,9 @@ __device__ void routed_down(const FfnArgs &a, int e, const Tokens<MAXM> &tk, int
     const int cp = lane % LPR, rsub = lane / LPR;
     const int H = a.H, I = a.I;
     const int64_t nb_row = I / MOE_QK, nb_mat = (int64_t)H * nb_row, NB = nb_mat * a.E;
+    int sig[MAXM];                                            // h of token t was stored as h * 2^-sig[t]
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) sig[m] = a.hsig[tk.tok[m < tk.n ? m : 0]];
     uint32_t hr[CPL][MAXM][32];
     float hsum[CPL][MAXM][4];
 #pragma unroll
@@ -977,7 +1028,7 @@ __device__ void routed_down(const FfnArgs &a, int e, const Tokens<MAXM> &tk, int
         const int r = row0 + (wv * NR + j) * RPI + rsub;
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) {
-            const float o = row_sum<LPR>(acc[m]);
+            const float o = ldexpf(row_sum<LPR>(acc[m]), sig[m]);
             if (m < tk.n && cp == 0 && r < H) a.slot_out[(int64_t)tk.slot[m] * H + r] = o;
         }
     }
@@ -1017,6 +1068,9 @@ __device__ void routed_down_q4k(const FfnArgs &a, int e, const Tokens<MAXM> &tk,
     const int cp = lane % LPR, rsub = lane / LPR;
     const int H = a.H, I = a.I;
     const int64_t nb_row = I / MOE_QK, nb_mat = (int64_t)H * nb_row, NB = nb_mat * a.E;
+    int sig[MAXM];                                            // h of token t was stored as h * 2^-sig[t]
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) sig[m] = a.hsig[tk.tok[m < tk.n ? m : 0]];
     uint32_t hr[CPL][MAXM][16];
     float hsum[CPL][MAXM];
 #pragma unroll
@@ -1063,7 +1117,7 @@ __device__ void routed_down_q4k(const FfnArgs &a, int e, const Tokens<MAXM> &tk,
         const int r = row0 + (wv * NR + jr) * RPI + rsub;
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) {
-            const float o = row_sum<LPR>(acc[m]);
+            const float o = ldexpf(row_sum<LPR>(acc[m]), sig[m]);
             if (m < tk.n && cp == 0 && r < H) a.slot_out[(int64_t)tk.slot[m] * H + r] = o;
         }
     }
@@ -1151,7 +1205,7 @@ template <int LPR, int CPL, int NR>
 __device__ __forceinline__ void down_rows_one(const FfnArgs &a, const uint4 (&q)[NR][CPL],
                                               const uint32_t (&sm)[NR][CPL], const uint32_t (&dd)[NR][CPL],
                                               const uint32_t (&hr)[CPL][1][32], const float (&hsum)[CPL][1][4],
-                                              int slot, int row0) {
+                                              int slot, int sig, int row0) {
     constexpr int RPI = 64 / LPR;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int cp = lane % LPR, rsub = lane / LPR;
@@ -1160,7 +1214,7 @@ __device__ __forceinline__ void down_rows_one(const FfnArgs &a, const uint4 (&q)
         float acc[1] = {0.f};
 #pragma unroll
         for (int i = 0; i < CPL; ++i) q2k_chunk<1>(q[j][i], sm[j][i], dd[j][i], hr[i], hsum[i], acc);
-        const float o = row_sum<LPR>(acc[0]);
+        const float o = ldexpf(row_sum<LPR>(acc[0]), sig);
         const int r = row0 + (wv * NR + j) * RPI + rsub;
         if (cp == 0 && r < a.H) a.slot_out[(int64_t)slot * a.H + r] = o;
     }
@@ -1199,7 +1253,7 @@ __device__ void routed_down_mt(const FfnArgs &a, int e, int o0, int ne, int row0
             dd[j][i] = D[bl];
         }
     }
-    down_rows_one<LPR, CPL, NR>(a, q, sm, dd, hr, hsum, tk.slot[0], row0);
+    down_rows_one<LPR, CPL, NR>(a, q, sm, dd, hr, hsum, tk.slot[0], a.hsig[tk.tok[0]], row0);
 #pragma unroll 1
     for (int m = 1; m < ne; ++m) {
 #pragma unroll
@@ -1218,7 +1272,7 @@ __device__ void routed_down_mt(const FfnArgs &a, int e, int o0, int ne, int row0
         float sm_h[CPL][1][4];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) load_h_chunk<1>(h, I, tm, cp + LPR * i, hm[i], sm_h[i]);
-        down_rows_one<LPR, CPL, NR>(a, q, sm, dd, hm, sm_h, tm.slot[0], row0);
+        down_rows_one<LPR, CPL, NR>(a, q, sm, dd, hm, sm_h, tm.slot[0], a.hsig[tm.tok[0]], row0);
     }
 }
 
@@ -1307,7 +1361,9 @@ constexpr int NR = 4;
 
 template <int FG, int MAXM, int LPR, int CPL, int SLPR, int SCPL>
 hipError_t run_gateup(const FfnArgs &a, int max_active, _Float16 *h, float *hs, hipStream_t st) {
-    const int rows = WAVES * NR * (64 / LPR);
+    // one q4k token over two chunks per lane: 3 rows per wave keep the kernel at 3 waves per SIMD
+    constexpr int NRG = (FG == FMT_Q4K && CPL == 2 && MAXM == 1) ? 3 : NR;
+    const int rows = WAVES * NRG * (64 / LPR);
     const int wpe = (a.I + rows - 1) / rows;
     const int nr = max_active * wpe;
     int ns = 0;
@@ -1315,7 +1371,7 @@ hipError_t run_gateup(const FfnArgs &a, int max_active, _Float16 *h, float *hs, 
         const int srows = WAVES * shared_nr<SCPL>() * (64 / SLPR);
         ns = (a.Is + srows - 1) / srows;
     }
-    hipLaunchKernelGGL((k_gemv_gateup<FG, LPR, CPL, SLPR, SCPL, MAXM, NR>), dim3(nr + ns), dim3(256), 0, st, a, wpe, nr,
+    hipLaunchKernelGGL((k_gemv_gateup<FG, LPR, CPL, SLPR, SCPL, MAXM, NRG>), dim3(nr + ns), dim3(256), 0, st, a, wpe, nr,
                        h, hs);
     return hipGetLastError();
 }
@@ -1455,16 +1511,21 @@ bool ffn_gemv_supported(const FfnArgs &a) {
     return false;
 }
 
+// workspace: h [T*k][I] fp16 | hs [T][Is] fp32 | hsig [T] int32, each 256-byte aligned
+static size_t gemv_h_bytes(int I, int k, int T) { return ((size_t)T * k * I * sizeof(_Float16) + 255) / 256 * 256; }
+static size_t gemv_hs_bytes(int Is, int T) { return ((size_t)T * Is * sizeof(float) + 255) / 256 * 256; }
+
 size_t ffn_workspace_gemv(int H, int I, int E, int k, int Is, int T) {
     (void)H; (void)E;
-    size_t hb = ((size_t)T * k * I * sizeof(_Float16) + 255) / 256 * 256;
-    return hb + (size_t)T * Is * sizeof(float) + 256;
+    return gemv_h_bytes(I, k, T) + gemv_hs_bytes(Is, T) + ((size_t)T * sizeof(int32_t) + 255) / 256 * 256;
 }
 
-hipError_t launch_ffn_gemv(const FfnArgs &a, hipStream_t st) {
-    _Float16 *h = static_cast<_Float16 *>(a.ws);
-    size_t hb = ((size_t)a.T * a.k * a.I * sizeof(_Float16) + 255) / 256 * 256;
-    float *hs = reinterpret_cast<float *>(static_cast<char *>(a.ws) + hb);
+hipError_t launch_ffn_gemv(const FfnArgs &args, hipStream_t st) {
+    FfnArgs a = args;
+    char *ws = static_cast<char *>(a.ws);
+    _Float16 *h = reinterpret_cast<_Float16 *>(ws);
+    float *hs = reinterpret_cast<float *>(ws + gemv_h_bytes(a.I, a.k, a.T));
+    a.hsig = reinterpret_cast<int32_t *>(ws + gemv_h_bytes(a.I, a.k, a.T) + gemv_hs_bytes(a.Is, a.T));
     if (a.T == 1) return dispatch<1>(a, h, hs, st);
     if (mt_ok(a)) return dispatch_mt(a, h, hs, st);
     return dispatch<4>(a, h, hs, st);

@@ -45,6 +45,7 @@ struct FfnArgs {
     int x_bf16;
     const int32_t *topk_idx, *offsets, *perm, *active;
     float *slot_out, *shared_out;
+    int32_t *hsig;                     // [T] exponent of the routed fp16 h per token (workspace; fp16-h kernels)
     void *ws;
     int stages;                        // bit 0: gate/up + SwiGLU, bit 1: down
 };

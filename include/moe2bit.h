@@ -177,11 +177,12 @@ size_t moe_expert_ffn_workspace(const moe_layer_desc *L, int32_t n_tokens);
  * above that) or fp32 (generic kernels); the shared expert's
  * h in fp32 (decode, generic) or as a bf16 hi + lo pair (grouped GEMM).  The
  * grouped-GEMM kernels read x as fp16 (exact for bf16 values in fp16 range).
- * Range: the fp16 h keeps the layer's 1e-3 accuracy while |h| stays in fp16's
- * normal range (about 6.1e-5 .. 65504).  h grows as |x|^2; normalized FFN
- * inputs sit well inside it (the tests cover x scaled by 2^-6 .. 2^6 around
- * unit RMS).  Inputs far outside lose accuracy (tiny) or overflow to inf/NaN
- * (huge); scale them into range first.
+ * Range: the fp16 h of token t is stored as h * 2^-s(t), where s(t) =
+ * 2 * (ilogb(max_c |x[t][c]|) - 1), clamped to [-100, 100] (0 for an all-zero
+ * row), and the down projection multiplies its sums by 2^s(t).  A power of two
+ * scales exactly, and h grows as |x|^2, so the stored h stays near unit scale
+ * for any input range; the tests cover x scaled by 2^-10 .. 2^12 around unit
+ * RMS.  Non-finite inputs give non-finite outputs.
  */
 moe_status moe_expert_ffn(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
                           const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
