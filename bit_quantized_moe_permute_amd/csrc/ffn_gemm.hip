@@ -270,6 +270,19 @@ __device__ __forceinline__ void gu_load(const FfnArgs &a, int e, int row, int kb
     }
 }
 
+// 4 * byte B of v in one instruction (sub-dword operand select): the byte offset of a 32-bit table entry
+template <int B> __device__ __forceinline__ uint32_t byte_x4(uint32_t v) {
+    uint32_t r;
+    if constexpr (B == 0) asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(v));
+    else if constexpr (B == 1) asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(v));
+    else if constexpr (B == 2) asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(v));
+    else asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(v));
+    return r;
+}
+__device__ __forceinline__ uint32_t lds_at(const uint32_t *tab, uint32_t byte_off) {
+    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(tab) + byte_off);
+}
+
 // One 256-wide K block: 16 K-steps x 2 B fragments x (1 or 2) token fragments.
 template <bool two>
 __device__ __forceinline__ void gu_block(const GuW &w, const uint4 *tile, const uint32_t *cb4, const uint32_t *sgn,
@@ -288,7 +301,9 @@ __device__ __forceinline__ void gu_block(const GuW &w, const uint4 *tile, const 
             mul[f][gi] = f16pair(iq2x_gscale(lo, hi) & keep);
         }
     }
-    // phase 1: all 32 codebook/sign lookups of the block at once (one LDS round trip)
+    // phase 1: all 32 codebook/sign lookups of the block at once (one LDS round trip); a field is the 16-bit
+    // half of a word: byte 0 the codebook row, byte 1 the sign index, each turned into a table byte offset by one
+    // sub-dword shift
     uint32_t words[2][16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -297,8 +312,8 @@ __device__ __forceinline__ void gu_block(const GuW &w, const uint4 *tile, const 
         for (int f = 0; f < 2; ++f) {
             const uint4 qq = w.q[f][chunk];
             const uint32_t dw = (fld >> 2) ? ((p < 2) ? qq.z : qq.w) : ((p < 2) ? qq.x : qq.y);
-            const uint32_t fw = (p & 1) ? (dw >> 16) : (dw & 0xFFFFu);
-            words[f][j] = cb4[fw & 0xFFu] | sgn[(fw >> 8) & 0x7Fu];
+            words[f][j] = (p & 1) ? (lds_at(cb4, byte_x4<2>(dw)) | lds_at(sgn, byte_x4<3>(dw)))
+                                  : (lds_at(cb4, byte_x4<0>(dw)) | lds_at(sgn, byte_x4<1>(dw)));
         }
     }
     // phase 2: convert and multiply on the matrix cores; A fragments read one K-step ahead
@@ -559,7 +574,10 @@ __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
     const FfnArgs &a = g.a;
     constexpr int RPI = FG == FMT_Q4K ? ROWS / 2 : ROWS;
     __shared__ int tile_off[257];
-    __shared__ uint32_t cb4[256], sgn[128];
+    // the tables are laid out first (largest alignment), below 64 KiB, so that their base address folds into the
+    // lookups' immediate offsets; sgn is indexed by a field's whole high byte (bit 7 is not a sign bit)
+    __shared__ __attribute__((aligned(64))) uint32_t cb4[256];
+    __shared__ __attribute__((aligned(64))) uint32_t sgn[256];
     __shared__ const uint16_t *src[TOK];
     __shared__ int dst[TOK];
     __shared__ float hfac[TOK];                                 // routed rows: 2^-sigma of the row's token
@@ -572,7 +590,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
     const int H = a.H;
     if (FG == FMT_IQ2X && !it.shared) {
         if (tid < 256) cb4[tid] = codebook_row_fp4(a.codebook, tid);
-        else if (tid < 384) sgn[tid - 256] = sign_spread(tid - 256);
+        else sgn[tid - 256] = sign_spread((tid - 256) & 0x7F);
     }
     if (tid < TOK) {
         const int m = tid < it.n ? tid : 0;                  // rows past the tile alias row 0
