@@ -397,11 +397,18 @@ __device__ __forceinline__ void q4_load(const uint8_t *W, int64_t NB, int64_t bl
     w.meta = *reinterpret_cast<const uint4 *>(W + NB * 128 + bl * 16);
 }
 
+// (v & m) | c in one instruction
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(m), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ f16x8_t q4_f16(uint32_t word, f16x2_t sc2, f16x2_t nsc2) {
     f16x8_t r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t t = ((word >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+        const uint32_t t = and_or(word >> (4 * i), 0x000F000Fu, 0x64006400u);
         const f16x2_t p = __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, t), sc2, nsc2);
         r[2 * i] = p.x;
         r[2 * i + 1] = p.y;
