@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "routed-MoE layer tokens/sec at decode B=1 and prefill; % of HBM/MFMA peak"
+PREFILL_SAMPLE = 8        # tokens per prefill workload checked against the oracle in the same run
 
 
 def log(msg):
@@ -331,8 +332,9 @@ def main():
     del g2
     torch.cuda.synchronize()
     prefill = None
+    samples = None if args.no_cpu_baseline else []      # prefill outputs for the oracle check
     if not args.no_prefill:
-        prefill = prefill_bench(L, layers[0], args.prefill_reps, ("prefill", "long"))
+        prefill = prefill_bench(L, layers[0], args.prefill_reps, ("prefill", "long"), samples)
 
     decode_q4k = None
     if not args.no_q4k:
@@ -357,7 +359,7 @@ def main():
                       "layer_copies": n4}
         log(f"decode q4k: {K / qwall:.0f} tokens/s")
         if not args.no_prefill:
-            prefill.update(prefill_bench(L4, layers4[0], args.prefill_reps, ("long_q4k",)))
+            prefill.update(prefill_bench(L4, layers4[0], args.prefill_reps, ("long_q4k",), samples))
         del layers4
         torch.cuda.synchronize()
 
@@ -370,7 +372,7 @@ def main():
             forward(layers[0], x[i: i + 1], pb)
             gy.append(pb.y.cpu().numpy()[0].astype(np.float64))
             gi.append(pb.topk_idx.cpu().numpy()[0].copy())
-        cpu = cpu_baseline(L, x_np, args.cpu_seconds, np.array(gy), np.array(gi))
+        cpu = cpu_baseline(L, x_np, args.cpu_seconds, np.array(gy), np.array(gi), samples or ())
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -437,14 +439,16 @@ def combine_bench(k, H, Ts, reps):
     return out
 
 
-def prefill_bench(L, DL, reps, names):
+def prefill_bench(L, DL, reps, names, samples=None):
     """Prefill workloads on layer DL: a 512-token chunk with a seeded per-expert
     router bias (skewed expert load, "prefill"), and the 11,709-token long
     prompt in 2048-token chunks (5 x 2048 + 1469; "long" with 2-bit experts,
     "long_q4k" with q4k experts).  Reported per workload:
     tokens/s over the whole prompt, and the gate/up grouped-GEMM stage (fp16
     copy of x + k_gemm_gateup) timed alone with HIP events against the bf16/fp16
-    MFMA peak, counting only the useful FLOPs (selected experts, real tokens)."""
+    MFMA peak, counting only the useful FLOPs (selected experts, real tokens).
+    With a list in samples, the GPU outputs of PREFILL_SAMPLE tokens spread over
+    the first chunk are appended to it for the oracle check of the same run."""
     import torch
 
     import synth
@@ -491,6 +495,12 @@ def prefill_bench(L, DL, reps, names):
         f1.record()
         torch.cuda.synchronize()
         gu_us = f0.elapsed_time(f1) * 1e3 / reps
+        if samples is not None:
+            # b.y and b.topk_idx still hold the first chunk's layer outputs (the stage loop rewrites only h)
+            rows = np.unique(np.linspace(0, n - 1, PREFILL_SAMPLE).astype(np.int64))
+            samples.append({"workload": name, "layer": L, "bias": bias, "rows": (c0 + rows).tolist(),
+                            "x": x[c0 + rows], "y": b.y.cpu().numpy()[rows].astype(np.float64),
+                            "idx": b.topk_idx.cpu().numpy()[rows]})
         flops = 4.0 * n * k * H * I + 4.0 * n * H * Is
         tflops = flops / (gu_us * 1e-6) / 1e12
         step_flops = 6.0 * T_total * k * H * I + 6.0 * T_total * H * Is
@@ -513,11 +523,14 @@ def prefill_bench(L, DL, reps, names):
     return out
 
 
-def cpu_baseline(L, x_np, budget_s, gpu_y, gpu_idx):
+def cpu_baseline(L, x_np, budget_s, gpu_y, gpu_idx, prefill_samples=()):
     """The oracle (binary64, plain C with OpenMP over rows) on a bounded sample of
     decode tokens, one call per token, until the time budget is spent.  The GPU
     layer's outputs for the same tokens (gpu_y, gpu_idx) are checked against the
-    oracle's after the timed loop: routing bit-exact, per-token relative L2."""
+    oracle's after the timed loop: routing bit-exact, per-token relative L2.
+    The prefill samples (sampled tokens of each prefill workload's first chunk,
+    with that workload's layer and router bias) are checked the same way,
+    outside the timed loop."""
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     sp = L.spec
@@ -535,11 +548,28 @@ def cpu_baseline(L, x_np, budget_s, gpu_y, gpu_idx):
     err = np.linalg.norm(gpu_y[:done] - want, axis=1) / np.linalg.norm(want, axis=1)
     idx_ok = bool(np.array_equal(gpu_idx[:done], np.concatenate([o["topk_idx"] for o in outs])))
     log(f"parity on the sample: routing exact {idx_ok}, max per-token rel L2 {err.max():.3e}")
+    prefill_parity = {}
+    for smp in prefill_samples:
+        Ls, sps = smp["layer"], smp["layer"].spec
+        ys, ids = [], []
+        for r in range(len(smp["rows"])):
+            o = oracle.layer(smp["x"][r: r + 1], Ls.w_router, sps.top_k, sps.n_experts, sps.inter, sps.gate_up_fmt,
+                             Ls.gate, Ls.up, sps.down_fmt, Ls.down, Ls.codebook, bias=smp["bias"], shared=Ls.shared)
+            ys.append(o["y"][0])
+            ids.append(o["topk_idx"][0])
+        ys, ids = np.array(ys), np.array(ids)
+        e = np.linalg.norm(smp["y"] - ys, axis=1) / np.linalg.norm(ys, axis=1)
+        ok = bool(np.array_equal(smp["idx"], ids))
+        prefill_parity[smp["workload"]] = {"tokens": len(smp["rows"]), "rows": smp["rows"], "routing_exact": ok,
+                                           "max_rel_l2": float(f"{e.max():.3e}"), "tolerance": 1e-3}
+        log(f"parity on {smp['workload']} (tokens {smp['rows']} of its first chunk): routing exact {ok}, "
+            f"max per-token rel L2 {e.max():.3e}")
     return {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {done} of the 1000 decode tokens, whole layer (route, permute, 8 routed experts, "
                       f"shared expert, combine) in binary64, {el:.1f} s",
             "parity": {"tokens": done, "routing_exact": idx_ok, "max_rel_l2": float(f"{err.max():.3e}"),
-                       "tolerance": 1e-3}}
+                       "tolerance": 1e-3},
+            "parity_prefill": prefill_parity}
 
 
 if __name__ == "__main__":
