@@ -271,7 +271,7 @@ moe_status moe_combine(const float *slot_out, const float *topk_w, const float *
                        int32_t top_k, int32_t hidden, float *y, void *stream) {
     if (!slot_out || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "moe_combine: null pointer");
     if (n_tokens < 1 || top_k < 1 || hidden < 1) return fail(MOE_ERR_INVALID_ARG, "moe_combine: bad shape");
-    if (!aligned(slot_out, 4) || !aligned(y, 4) || !aligned(topk_w, 4))
+    if (!aligned(slot_out, 4) || !aligned(y, 4) || !aligned(topk_w, 4) || (shared_out && !aligned(shared_out, 4)))
         return fail(MOE_ERR_INVALID_ARG, "moe_combine: misaligned pointer");
     return from_hip(moe::launch_combine(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, y, (hipStream_t)stream),
                     "moe_combine");

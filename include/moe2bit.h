@@ -206,8 +206,17 @@ moe_status moe_expert_down(const moe_layer_desc *L, const void *x, int32_t x_dt,
                            void *stream);
 
 /*
- * y[t][c] = sum_{j<k} topk_w[t][j] * slot_out[t*k+j][c] (+ shared_out[t][c]),
- * j in increasing order, fp32.  shared_out may be NULL.
+ * Top-k weighted combine that closes the layer (the sum in the formula at the
+ * top of this file):
+ *   y[t][c] = sum_{j<k} topk_w[t][j] * slot_out[t*k+j][c] (+ shared_out[t][c]),
+ * fp32: fused multiply-adds from 0 in increasing j, the shared term added last.
+ *   slot_out   [n_tokens*top_k][hidden] fp32 in slot order (moe_expert_ffn);
+ *   topk_w     [n_tokens][top_k] fp32 (moe_route);
+ *   shared_out [n_tokens][hidden] fp32, or NULL for a layer without one;
+ *   y          [n_tokens][hidden] fp32, written; must not alias an input.
+ * Rows with hidden % 4 == 0 and 16-byte aligned pointers take 16-byte loads;
+ * the arithmetic is the same either way.  Returns MOE_ERR_INVALID_ARG for a
+ * NULL slot_out, topk_w or y, a bad shape or a pointer not 4-byte aligned.
  */
 moe_status moe_combine(const float *slot_out, const float *topk_w, const float *shared_out, int32_t n_tokens,
                        int32_t top_k, int32_t hidden, float *y, void *stream);

@@ -132,6 +132,8 @@ def test_prepare_and_combine_reject_bad_arguments(lib):
     g.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]
     assert g(None, vp(0x1000), None, 1, 8, 4096, vp(0x1000), None) == 1
     assert g(vp(0x1000), vp(0x1000), None, 0, 8, 4096, vp(0x1000), None) == 1
+    assert g(vp(0x1000), vp(0x1000), vp(0x1002), 1, 8, 4096, vp(0x1000), None) == 1   # misaligned shared output
+    assert "misaligned" in _err(lib)
     h = lib.moe_combine_steer
     h.restype = ctypes.c_int
     h.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_float, vp, vp]
