@@ -92,8 +92,27 @@ def _check(st: int):
         raise MoeError(st, lib.moe_last_error().decode())
 
 
-def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+def _ptr(t, dtype=None):
+    """Device pointer of a contiguous GPU tensor (None passes through); dtype, when given, is checked."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise TypeError("expected a GPU tensor (the library takes device pointers)")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32(t):
+    import torch
+    return _ptr(t, torch.int32)
+
+
+def _f32(t):
+    import torch
+    return _ptr(t, torch.float32)
 
 
 def _stream(stream):
@@ -133,7 +152,7 @@ def moe_prepare_weights(fmt, n_mats, rows, cols, canonical, prepared, stream=Non
 
 def moe_dequantize(fmt, prepared, n_mats, rows, cols, mat_begin, mat_count, codebook, out, stream=None):
     _check(lib.moe_dequantize(fmt, _ptr(prepared), n_mats, rows, cols, mat_begin, mat_count, _ptr(codebook),
-                              _ptr(out), _stream(stream)))
+                              _f32(out), _stream(stream)))
 
 
 def moe_route_workspace(n_tokens: int, n_experts: int, top_k: int) -> int:
@@ -143,8 +162,8 @@ def moe_route_workspace(n_tokens: int, n_experts: int, top_k: int) -> int:
 def moe_route(x, w_router, n_experts, top_k, topk_idx, topk_w, expert_offsets, perm, active, ws, bias=None,
               logits=None, stream=None):
     T, H = x.shape
-    _check(lib.moe_route(_ptr(x), _dt(x), T, H, _ptr(w_router), _dt(w_router), n_experts, _ptr(bias), top_k,
-                         _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(expert_offsets), _ptr(perm), _ptr(active),
+    _check(lib.moe_route(_ptr(x), _dt(x), T, H, _ptr(w_router), _dt(w_router), n_experts, _f32(bias), top_k,
+                         _i32(topk_idx), _f32(topk_w), _f32(logits), _i32(expert_offsets), _i32(perm), _i32(active),
                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
@@ -154,31 +173,31 @@ def moe_expert_ffn_workspace(desc: LayerDesc, n_tokens: int) -> int:
 
 def moe_expert_ffn(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, slot_out, shared_out, ws, stream=None):
     T = x.shape[0]
-    _check(lib.moe_expert_ffn(ctypes.byref(desc), _ptr(x), _dt(x), T, _ptr(topk_idx), _ptr(expert_offsets),
-                              _ptr(perm), _ptr(active), _ptr(slot_out), _ptr(shared_out), _ptr(ws),
+    _check(lib.moe_expert_ffn(ctypes.byref(desc), _ptr(x), _dt(x), T, _i32(topk_idx), _i32(expert_offsets),
+                              _i32(perm), _i32(active), _f32(slot_out), _f32(shared_out), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_expert_gate_up(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, ws, stream=None):
-    _check(lib.moe_expert_gate_up(ctypes.byref(desc), _ptr(x), _dt(x), x.shape[0], _ptr(topk_idx),
-                                  _ptr(expert_offsets), _ptr(perm), _ptr(active), _ptr(ws),
+    _check(lib.moe_expert_gate_up(ctypes.byref(desc), _ptr(x), _dt(x), x.shape[0], _i32(topk_idx),
+                                  _i32(expert_offsets), _i32(perm), _i32(active), _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_expert_down(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, slot_out, shared_out, ws, stream=None):
-    _check(lib.moe_expert_down(ctypes.byref(desc), _ptr(x), _dt(x), x.shape[0], _ptr(topk_idx),
-                               _ptr(expert_offsets), _ptr(perm), _ptr(active), _ptr(slot_out), _ptr(shared_out),
+    _check(lib.moe_expert_down(ctypes.byref(desc), _ptr(x), _dt(x), x.shape[0], _i32(topk_idx),
+                               _i32(expert_offsets), _i32(perm), _i32(active), _f32(slot_out), _f32(shared_out),
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_combine(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, y, stream=None):
-    _check(lib.moe_combine(_ptr(slot_out), _ptr(topk_w), _ptr(shared_out), n_tokens, top_k, hidden, _ptr(y),
+    _check(lib.moe_combine(_f32(slot_out), _f32(topk_w), _f32(shared_out), n_tokens, top_k, hidden, _f32(y),
                            _stream(stream)))
 
 
 def moe_combine_steer(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, steer_v, steer_f, y, stream=None):
-    _check(lib.moe_combine_steer(_ptr(slot_out), _ptr(topk_w), _ptr(shared_out), n_tokens, top_k, hidden,
-                                 _ptr(steer_v), float(steer_f), _ptr(y), _stream(stream)))
+    _check(lib.moe_combine_steer(_f32(slot_out), _f32(topk_w), _f32(shared_out), n_tokens, top_k, hidden,
+                                 _f32(steer_v), float(steer_f), _f32(y), _stream(stream)))
 
 
 from .layer import DeviceLayer, LayerBuffers  # noqa: E402  (needs `lib` loaded)

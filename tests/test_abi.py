@@ -39,6 +39,15 @@ def test_binding_lists_the_same_symbols():
     assert sorted(re.findall(r'"(moe_\w+)"', exported)) == declared_functions()
 
 
+def test_binding_rejects_host_tensors():
+    """The binding takes device tensors only; a host tensor fails before any library call."""
+    torch = pytest.importorskip("torch")
+    import bit_quantized_moe_permute_amd as m
+    t = torch.zeros(8, 64)
+    with pytest.raises(TypeError):
+        m.moe_combine(t, torch.ones(1, 8), None, 1, 8, 64, torch.empty(1, 64))
+
+
 def test_abi_version(lib):
     lib.moe_abi_version.restype = ctypes.c_int
     hdr = open(HDR).read()

@@ -343,6 +343,26 @@ def test_combine_matches_numpy(m):
         assert rel_l2_rows(y.cpu().numpy(), want).max() <= 1e-6
 
 
+def test_binding_rejects_strided_and_mistyped_tensors(m):
+    """The binding hands raw device pointers to the library, so it refuses tensors the kernels would misread."""
+    note("binding argument checks")
+    o = torch.zeros(8, 64, device="cuda")
+    w = torch.ones(1, 8, device="cuda")
+    y = torch.empty(1, 64, device="cuda")
+    with pytest.raises(ValueError):
+        m.moe_combine(o.t().contiguous().t(), w, None, 1, 8, 64, y)      # transposed view: not contiguous
+    with pytest.raises(TypeError):
+        m.moe_combine(o, w.double(), None, 1, 8, 64, y)                  # weights must be fp32
+    with pytest.raises(TypeError):
+        m.moe_combine(o.cpu(), w, None, 1, 8, 64, y)                     # host memory
+    idx64 = torch.zeros(1, 8, dtype=torch.int64, device="cuda")
+    with pytest.raises(TypeError):
+        m.moe_route(torch.zeros(1, 256, device="cuda"), torch.zeros(8, 256, device="cuda"), 8, 8, idx64, w,
+                    torch.zeros(9, dtype=torch.int32, device="cuda"), torch.zeros(8, dtype=torch.int32, device="cuda"),
+                    torch.zeros(9, dtype=torch.int32, device="cuda"), torch.zeros(1024, dtype=torch.uint8,
+                                                                                  device="cuda"))
+
+
 # ----------------------------------------------------------------------------
 # directional steering fused into the combine
 # ----------------------------------------------------------------------------
