@@ -192,10 +192,11 @@ moe_status moe_expert_ffn(const moe_layer_desc *L, const void *x, int32_t x_dt, 
 /*
  * The two halves of moe_expert_ffn, for callers that schedule them apart (or
  * time them): moe_expert_gate_up writes the SwiGLU activations h of every slot
- * and of the shared expert into `ws` (layout private to the library);
- * moe_expert_down reads them from the same `ws` and writes slot_out and
- * shared_out.  Same arguments and checks as moe_expert_ffn; both calls must
- * see the same L, x, n_tokens, routing arrays and ws.
+ * and of the shared expert, with the per-token scale exponents of the fp16 h,
+ * into `ws` (layout private to the library); moe_expert_down reads them from
+ * the same `ws` and writes slot_out and shared_out.  Same arguments and checks
+ * as moe_expert_ffn; both calls must see the same L, x, n_tokens, routing
+ * arrays and ws, and ws must not be written in between.
  */
 moe_status moe_expert_gate_up(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
                               const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
