@@ -543,3 +543,32 @@ def test_layer_activation_scales(m, scale_exp, T):
     err = rel_l2_rows(got["y"], ref["y"])
     note(f"  max per-token rel L2 = {err.max():.3e}")
     assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("name", ["small", "small_q4k"])
+@pytest.mark.parametrize("T,path", [(1, 0), (3, 0), (3, 3), (37, 0)])
+def test_layer_zero_spike_and_mixed_scale_tokens(m, name, T, path):
+    """One call mixing an all-zero token, a one-hot spike token (a single 64.0) and tokens scaled by 2^-10 and
+    2^12 next to unit-scale ones: each token carries its own h scale, also inside a shared grouped-GEMM token
+    tile, and the zero token's output is exactly zero."""
+    note(f"zero / spike / mixed-scale tokens {name} T={T} path={path}")
+    L = _layer(name)
+    sp = L.spec
+    xf = synth.bf16_bits_to_f32(synth.activations(name, T, sp.hidden, True, seed=990 + T)).copy()
+    xf[0] = 0.0
+    if T > 1:
+        xf[1] = 0.0
+        xf[1, 7] = 64.0
+    if T > 2:
+        xf[2] *= np.float32(2.0 ** -10)
+    if T > 3:
+        xf[3] *= np.float32(2.0 ** 12)
+    x = synth.to_bf16_bits(xf)
+    got = _run_layer(m, L, x, path)
+    ref = _oracle_layer(L, x)
+    assert np.array_equal(got["topk_idx"], ref["topk_idx"])
+    assert not np.any(got["y"][0]), "an all-zero token must give an all-zero output"
+    assert rel_l2_rows(got["slot_out"], ref["slot_out"]).max() <= TOL
+    err = rel_l2_rows(got["y"], ref["y"])
+    note(f"  max per-token rel L2 = {err.max():.3e}")
+    assert err.max() <= TOL
