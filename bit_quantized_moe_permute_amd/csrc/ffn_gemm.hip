@@ -158,9 +158,10 @@ __device__ __forceinline__ int tpos(int m, int c) { return m * 32 + (c ^ (m & 15
 // Tiles are staged through registers: x_fetch issues the global loads of a
 // tile (4 x 16 B per thread, 32 consecutive threads per 512-byte row), the
 // compute of the current tile runs, then x_store writes the registers to LDS.
-struct XStage {
-    uint4 v[4];
+template <int NV> struct XStageN {
+    uint4 v[NV];                 // NV x 16 B per thread: the first 16 * NV rows of a tile
 };
+using XStage = XStageN<4>;
 
 // Row pointers are read back from LDS, so the compiler cannot tell they point
 // to global memory; loading through a flat pointer would tie the loads to the
@@ -173,9 +174,10 @@ __device__ __forceinline__ uint4 gload16(const uint16_t *p) {
 }
 
 // src_row[m]: start of row m (rows past the tile's tokens alias row 0); k0: first column
-__device__ __forceinline__ void x_fetch(const uint16_t *const *src_row, int k0, XStage &xs) {
+template <int NV>
+__device__ __forceinline__ void x_fetch(const uint16_t *const *src_row, int k0, XStageN<NV> &xs) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NV; ++i) {
         const int idx = threadIdx.x + NTHR * i, m = idx >> 5, c = idx & 31;
         xs.v[i] = gload16(src_row[m] + k0 + 8 * c);
     }
@@ -192,9 +194,9 @@ __device__ __forceinline__ void x_fetch_hilo(const uint16_t *const *hi, const ui
     }
 }
 
-__device__ __forceinline__ void x_store(const XStage &xs, uint4 *tile) {
+template <int NV> __device__ __forceinline__ void x_store(const XStageN<NV> &xs, uint4 *tile) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NV; ++i) {
         const int idx = threadIdx.x + NTHR * i, m = idx >> 5, c = idx & 31;
         tile[tpos(m, c)] = xs.v[i];
     }
@@ -350,7 +352,7 @@ __device__ __forceinline__ void gu_loop(const FfnArgs &a, int e, int row, int hh
     const int H = a.H, nkb = H / KB;
     const int64_t nb_row = H / KB, nb_mat = (int64_t)a.I * nb_row, NB = nb_mat * a.E;
     GuW w0, w1;
-    XStage xs;
+    XStageN<two ? 4 : 2> xs;                             // a one-fragment tile needs its first 32 rows only
     x_fetch(src, 0, xs);
     gu_load(a, e, row, 0, hh, nb_row, nb_mat, NB, w0);
     x_store(xs, tiles[0]);
