@@ -421,9 +421,10 @@ __device__ __forceinline__ f16x8_t q4_f16(uint32_t word, f16x2_t sc2, f16x2_t ns
 // Store a fetched tile to LDS and its per-32 sums to hs (hs[m] = {hi 0..3,
 // lo 0..3, hi 4..7, lo 4..7}).  The four chunks of a sub-block sit in four
 // consecutive lanes; they reduce with two cross-lane steps.
-__device__ __forceinline__ void x_store_sums32(const XStage &xs, uint4 *tile, _Float16 (*hs)[16]) {
+template <int NV>
+__device__ __forceinline__ void x_store_sums32(const XStageN<NV> &xs, uint4 *tile, _Float16 (*hs)[16]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NV; ++i) {
         const int idx = threadIdx.x + NTHR * i, m = idx >> 5, c = idx & 31;
         tile[tpos(m, c)] = xs.v[i];
         const uint32_t wds[4] = {xs.v[i].x, xs.v[i].y, xs.v[i].z, xs.v[i].w};
@@ -488,7 +489,7 @@ __device__ __forceinline__ void q4_loop(const uint8_t *W, int64_t NB, int64_t bl
                                         _Float16 (*hs)[TOK][16], float &dprev, float &mprev, f32x16_t (&acc)[2],
                                         f32x16_t (&accm)[2]) {
     Q4W w0, w1;
-    XStage xs;
+    XStageN<two ? 4 : 2> xs;                             // a one-fragment tile needs its first 32 rows only
     x_fetch(src, 0, xs);
     q4_load(W, NB, bl0, hh, w0);
     x_store_sums32(xs, tiles[0], hs[0]);
@@ -783,7 +784,7 @@ __device__ __forceinline__ void dn_loop(const FfnArgs &a, int e, int row, int hh
     const int I = a.I, H = a.H, nkb = I / KB;
     const int64_t nb_row = I / KB, nb_mat = (int64_t)H * nb_row, NB = nb_mat * a.E;
     DnW w0, w1;
-    XStage xs;
+    XStageN<two ? 4 : 2> xs;                             // a one-fragment tile needs its first 32 rows only
     x_fetch(src, 0, xs);
     dn_load(a, e, row, 0, hh, nb_row, nb_mat, NB, w0);
     x_store(xs, tiles[0]);
