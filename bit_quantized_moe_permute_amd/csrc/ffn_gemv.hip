@@ -477,6 +477,9 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    // whole workgroup, fewer experts than launched: leave before the weight requests (their address waits for
+    // the same scalar load as this count)
+    if (ai >= n_active) return;
     // --- all weights of this wave: units u = (row block u / 2, K block u % 2)
     const int64_t nb_row = H / MOE_QK, nb_mat = (int64_t)I * nb_row, NB = nb_mat * a.E;
     uint4 wq[2 * MF_RB][2];                                  // [unit][matrix]: chunk qd of the block
@@ -508,7 +511,6 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
         }
         wave_max_to(x_to_pieces(xv[m], tid, xq[m][0], xq[m][1], xsc[m]), xmx[m]);
     }
-    if (ai >= n_active) return;                               // whole workgroup: fewer experts than launched
     // --- every token of the call is multiplied (the products hold MAXM
     // tokens whichever are routed here); the expert's own tokens are picked
     // in the epilogue, so no routing load waits behind the weight stream.
@@ -662,6 +664,7 @@ __device__ __forceinline__ void routed_gateup_mt(const FfnArgs &a, const int32_t
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    if (ai >= n_active) return;                               // whole workgroup, before the weight requests
     const int64_t nb_row = H / MOE_QK, nb_mat = (int64_t)I * nb_row, NB = nb_mat * a.E;
     uint4 wq[2 * MF_RB][2];
     uint32_t wd[2 * MF_RB];
@@ -681,7 +684,6 @@ __device__ __forceinline__ void routed_gateup_mt(const FfnArgs &a, const int32_t
         if (row < 256) cb4[row] = cbrow_fp4(cbrow[i].x, cbrow[i].y);
         if (row < 256) sgn[row] = sign_spread(row & 0x7F);
     }
-    if (ai >= n_active) return;                               // whole workgroup
     wave_max_to(x_to_pieces(xv0, tid, xq[0][0], xq[0][1], xsc[0]), xmx[0]);
     if (s1 >= 0) wave_max_to(x_to_pieces(xv1, tid, xq[1][0], xq[1][1], xsc[1]), xmx[1]);
     else if ((tid & 3) == 0) xsc[1][tid >> 2] = 0.f;
