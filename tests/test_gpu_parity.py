@@ -259,6 +259,30 @@ def test_layer_matches_oracle(m, name, T, path):
     assert err.max() <= TOL
 
 
+@pytest.mark.parametrize("name,T,path", [("small", 1, 0), ("small", 3, 0), ("small", 37, 0), ("small_q4k", 3, 0),
+                                         ("small", 5, 3), ("tiny", 4, 0)])
+def test_split_ffn_calls_match_the_fused_call(m, name, T, path):
+    """moe_expert_gate_up then moe_expert_down, with their own workspace, give the same bits as moe_expert_ffn
+    (decode, verify, grouped-GEMM and generic kernels): the halves carry h and its per-token scale exponents
+    through the workspace."""
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers
+    note(f"split FFN calls {name} T={T} path={path}")
+    L = _layer(name)
+    sp = L.spec
+    DL = DeviceLayer.from_synth(L, path=path)
+    x = dev_x(synth.activations(name, T, sp.hidden, sp.x_bf16, seed=1300 + T))
+    b1, b2 = LayerBuffers.allocate(DL, T), LayerBuffers.allocate(DL, T)
+    m.moe_route(x, DL.w_router, DL.E, DL.k, b1.topk_idx, b1.topk_w, b1.offsets, b1.perm, b1.active, b1.ws_route,
+                bias=DL.bias)
+    m.moe_expert_ffn(DL.desc, x, b1.topk_idx, b1.offsets, b1.perm, b1.active, b1.slot_out, b1.shared_out, b1.ws_ffn)
+    m.moe_expert_gate_up(DL.desc, x, b1.topk_idx, b1.offsets, b1.perm, b1.active, b2.ws_ffn)
+    m.moe_expert_down(DL.desc, x, b1.topk_idx, b1.offsets, b1.perm, b1.active, b2.slot_out, b2.shared_out, b2.ws_ffn)
+    torch.cuda.synchronize()
+    assert torch.equal(b1.slot_out, b2.slot_out)
+    if b1.shared_out is not None:
+        assert torch.equal(b1.shared_out, b2.shared_out)
+
+
 @pytest.mark.parametrize("name,T", [("decode", 1), ("decode", 3), ("decode", 8), ("long_q4k", 1),
                                     ("long_q4k", 3)])
 def test_decode_layer_full_size(m, name, T):
