@@ -259,6 +259,35 @@ def test_layer_matches_oracle(m, name, T, path):
     assert err.max() <= TOL
 
 
+def test_two_streams_at_once_match_sequential_calls(m):
+    """The library keeps no state between calls: two layer calls (grouped GEMM at 37 tokens, verify kernels at 3)
+    running at once on two streams, each with its own buffers, give the bits of the same calls run one after the
+    other."""
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward
+    note("two streams at once")
+    L = _layer("small")
+    sp = L.spec
+    DL = DeviceLayer.from_synth(L)
+    xa = dev_x(synth.activations("small", 37, sp.hidden, True, seed=1400))
+    xb = dev_x(synth.activations("small", 3, sp.hidden, True, seed=1401))
+    ra, rb = LayerBuffers.allocate(DL, 37), LayerBuffers.allocate(DL, 3)
+    forward(DL, xa, ra)
+    forward(DL, xb, rb)
+    torch.cuda.synchronize()
+    ba, bb = LayerBuffers.allocate(DL, 37), LayerBuffers.allocate(DL, 3)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()           # default priority
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            forward(DL, xa, ba)
+        with torch.cuda.stream(s2):
+            forward(DL, xb, bb)
+    torch.cuda.synchronize()
+    assert torch.equal(ba.y, ra.y)
+    assert torch.equal(bb.y, rb.y)
+
+
 @pytest.mark.parametrize("name,T,path", [("small", 1, 0), ("small", 3, 0), ("small", 37, 0), ("small_q4k", 3, 0),
                                          ("small", 5, 3), ("tiny", 4, 0)])
 def test_split_ffn_calls_match_the_fused_call(m, name, T, path):
