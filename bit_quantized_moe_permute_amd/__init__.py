@@ -24,7 +24,7 @@ ABI_VERSION = 2
 EXPORTS = [
     "moe_abi_version", "moe_last_error", "moe_weight_bytes", "moe_prepare_weights", "moe_dequantize",
     "moe_route_workspace", "moe_route", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_expert_gate_up",
-    "moe_expert_down", "moe_combine", "moe_combine_steer",
+    "moe_expert_down", "moe_combine", "moe_combine_steer", "moe_probe_stream_read",
 ]
 
 
@@ -79,6 +79,8 @@ def _load():
     L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
     L.moe_combine_steer.restype = ctypes.c_int
     L.moe_combine_steer.argtypes = [vp, vp, vp, i32, i32, i32, vp, ctypes.c_float, vp, vp]
+    L.moe_probe_stream_read.restype = ctypes.c_int
+    L.moe_probe_stream_read.argtypes = [vp, sz, vp, i32, vp]
     if L.moe_abi_version() != ABI_VERSION:
         raise ImportError(f"libmoe2bit ABI {L.moe_abi_version()} != binding ABI {ABI_VERSION}")
     return L
@@ -122,6 +124,27 @@ def _stream(stream):
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _need(t, n: int, what: str):
+    """Host-side size check before a device pointer is handed to the library: the kernels index t up to n
+    elements (None passes)."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{what}: {t.numel()} elements, the call needs {n}")
+
+
+def _need_bytes(t, n: int, what: str):
+    if t is not None and t.numel() * t.element_size() < n:
+        raise ValueError(f"{what}: {t.numel() * t.element_size()} bytes, the call needs {n}")
+
+
+def _rows(x, hidden: int | None = None):
+    """(T, H) of a [T][H] activation tensor."""
+    if x.dim() != 2:
+        raise ValueError(f"activations must be [tokens][hidden], got shape {tuple(x.shape)}")
+    if hidden is not None and x.shape[1] != hidden:
+        raise ValueError(f"activations have {x.shape[1]} columns, the layer has hidden {hidden}")
+    return x.shape[0], x.shape[1]
+
+
 def _dt(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
@@ -147,10 +170,17 @@ def moe_weight_bytes(fmt: int, n_mats: int, rows: int, cols: int) -> int:
 
 
 def moe_prepare_weights(fmt, n_mats, rows, cols, canonical, prepared, stream=None):
+    nb = moe_weight_bytes(fmt, n_mats, rows, cols)
+    _need_bytes(canonical, nb, "canonical")
+    _need_bytes(prepared, nb, "prepared")
     _check(lib.moe_prepare_weights(fmt, n_mats, rows, cols, _ptr(canonical), _ptr(prepared), _stream(stream)))
 
 
 def moe_dequantize(fmt, prepared, n_mats, rows, cols, mat_begin, mat_count, codebook, out, stream=None):
+    _need_bytes(prepared, moe_weight_bytes(fmt, n_mats, rows, cols), "prepared")
+    _need(out, max(mat_count, 0) * rows * cols, "out")
+    if fmt == FMT_IQ2X:
+        _need_bytes(codebook, 256 * 8, "codebook")
     _check(lib.moe_dequantize(fmt, _ptr(prepared), n_mats, rows, cols, mat_begin, mat_count, _ptr(codebook),
                               _f32(out), _stream(stream)))
 
@@ -161,7 +191,16 @@ def moe_route_workspace(n_tokens: int, n_experts: int, top_k: int) -> int:
 
 def moe_route(x, w_router, n_experts, top_k, topk_idx, topk_w, expert_offsets, perm, active, ws, bias=None,
               logits=None, stream=None):
-    T, H = x.shape
+    T, H = _rows(x)
+    if w_router.dim() != 2 or tuple(w_router.shape) != (n_experts, H):
+        raise ValueError(f"w_router must be [{n_experts}][{H}], got shape {tuple(w_router.shape)}")
+    _need(topk_idx, T * top_k, "topk_idx")
+    _need(topk_w, T * top_k, "topk_w")
+    _need(expert_offsets, n_experts + 1, "expert_offsets")
+    _need(perm, T * top_k, "perm")
+    _need(active, n_experts + 1, "active")
+    _need(bias, n_experts, "bias")
+    _need(logits, T * n_experts, "logits")
     _check(lib.moe_route(_ptr(x), _dt(x), T, H, _ptr(w_router), _dt(w_router), n_experts, _f32(bias), top_k,
                          _i32(topk_idx), _f32(topk_w), _f32(logits), _i32(expert_offsets), _i32(perm), _i32(active),
                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
@@ -171,33 +210,68 @@ def moe_expert_ffn_workspace(desc: LayerDesc, n_tokens: int) -> int:
     return lib.moe_expert_ffn_workspace(ctypes.byref(desc), n_tokens)
 
 
+def _routing_sizes(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active):
+    T, _ = _rows(x, desc.hidden)
+    _need(topk_idx, T * desc.top_k, "topk_idx")
+    _need(expert_offsets, desc.n_experts + 1, "expert_offsets")
+    _need(perm, T * desc.top_k, "perm")
+    _need(active, desc.n_experts + 1, "active")
+    return T
+
+
+def _output_sizes(desc: LayerDesc, T: int, slot_out, shared_out):
+    _need(slot_out, T * desc.top_k * desc.hidden, "slot_out")
+    _need(shared_out, T * desc.hidden, "shared_out")
+
+
 def moe_expert_ffn(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, slot_out, shared_out, ws, stream=None):
-    T = x.shape[0]
+    T = _routing_sizes(desc, x, topk_idx, expert_offsets, perm, active)
+    _output_sizes(desc, T, slot_out, shared_out)
     _check(lib.moe_expert_ffn(ctypes.byref(desc), _ptr(x), _dt(x), T, _i32(topk_idx), _i32(expert_offsets),
                               _i32(perm), _i32(active), _f32(slot_out), _f32(shared_out), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_expert_gate_up(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, ws, stream=None):
+    _routing_sizes(desc, x, topk_idx, expert_offsets, perm, active)
     _check(lib.moe_expert_gate_up(ctypes.byref(desc), _ptr(x), _dt(x), x.shape[0], _i32(topk_idx),
                                   _i32(expert_offsets), _i32(perm), _i32(active), _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_expert_down(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, slot_out, shared_out, ws, stream=None):
+    T = _routing_sizes(desc, x, topk_idx, expert_offsets, perm, active)
+    _output_sizes(desc, T, slot_out, shared_out)
     _check(lib.moe_expert_down(ctypes.byref(desc), _ptr(x), _dt(x), x.shape[0], _i32(topk_idx),
                                _i32(expert_offsets), _i32(perm), _i32(active), _f32(slot_out), _f32(shared_out),
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def _combine_sizes(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, y):
+    _need(slot_out, n_tokens * top_k * hidden, "slot_out")
+    _need(topk_w, n_tokens * top_k, "topk_w")
+    _need(shared_out, n_tokens * hidden, "shared_out")
+    _need(y, n_tokens * hidden, "y")
+
+
 def moe_combine(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, y, stream=None):
+    _combine_sizes(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, y)
     _check(lib.moe_combine(_f32(slot_out), _f32(topk_w), _f32(shared_out), n_tokens, top_k, hidden, _f32(y),
                            _stream(stream)))
 
 
 def moe_combine_steer(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, steer_v, steer_f, y, stream=None):
+    _combine_sizes(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, y)
+    _need(steer_v, hidden, "steer_v")
     _check(lib.moe_combine_steer(_f32(slot_out), _f32(topk_w), _f32(shared_out), n_tokens, top_k, hidden,
                                  _f32(steer_v), float(steer_f), _f32(y), _stream(stream)))
+
+
+def moe_probe_stream_read(buf, nbytes, sink, n_blocks, stream=None):
+    """Measurement helper: one streaming read of buf's first nbytes bytes (sink: n_blocks uint32 words)."""
+    _need_bytes(buf, nbytes, "buf")
+    _need_bytes(sink, 4 * n_blocks, "sink")
+    _check(lib.moe_probe_stream_read(_ptr(buf), nbytes, _ptr(sink), n_blocks, _stream(stream)))
 
 
 from .layer import DeviceLayer, LayerBuffers  # noqa: E402  (needs `lib` loaded)

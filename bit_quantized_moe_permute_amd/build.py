@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe2bit.so")
-SOURCES = ["api.cpp", "prep.hip", "route.hip", "ffn_generic.hip", "ffn_gemv.hip", "ffn_gemm.hip", "combine.hip"]
+SOURCES = ["api.cpp", "prep.hip", "route.hip", "ffn_generic.hip", "ffn_gemv.hip", "ffn_gemm.hip", "combine.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

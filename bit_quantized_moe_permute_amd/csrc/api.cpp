@@ -291,4 +291,14 @@ moe_status moe_combine_steer(const float *slot_out, const float *topk_w, const f
                     "moe_combine_steer");
 }
 
+moe_status moe_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t n_blocks, void *stream) {
+    if (!buf || !sink) return fail(MOE_ERR_INVALID_ARG, "moe_probe_stream_read: null pointer");
+    if (bytes < 16 || bytes % 16 || !aligned(buf, 16) || !aligned(sink, 4))
+        return fail(MOE_ERR_INVALID_ARG, "moe_probe_stream_read: need a 16-byte aligned, non-empty multiple of 16 bytes");
+    if (n_blocks < 1 || n_blocks > (1 << 20))
+        return fail(MOE_ERR_INVALID_ARG, "moe_probe_stream_read: n_blocks outside [1, 2^20]");
+    return from_hip(moe::launch_stream_read(buf, (int64_t)bytes, sink, n_blocks, (hipStream_t)stream),
+                    "moe_probe_stream_read");
+}
+
 }  // extern "C"

@@ -15,9 +15,13 @@
 // B = the 4-bit mins), scaled the same way by dmin.  The shared expert runs in
 // the same launches with bf16 operands (x as is; h kept as bf16 hi + lo).
 //
-// Activations: the routed gate/up GEMM takes x converted to fp16 (exact for
-// 2^-14 <= |x| <= 65504; smaller magnitudes round to fp16 subnormals); h is
-// written in fp16.
+// Activations: the routed gate/up GEMM takes x converted to fp16 after a
+// per-token power-of-two prescale, x16 = x * 2^-e(t) with e(t) = ilogb(max_c
+// |x[t][c]|) - 1 (clamped to [-50, 50]), so every row's largest magnitude
+// lies in [2, 4) and no finite bf16 row overflows fp16; the epilogue
+// multiplies the gate and up sums by 2^e(t) before the SwiGLU (exact).  h is
+// written in fp16 as h * 2^-2e(t), and the down projection multiplies its
+// sums by 2^2e(t).
 //
 // Work mapping: workgroups are dealt round-robin to the 8 XCDs; items are
 // renumbered so that each XCD gets a contiguous run of items, and items are
@@ -591,6 +595,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
     __shared__ const uint16_t *src[TOK];
     __shared__ int dst[TOK];
     __shared__ float hfac[TOK];                                 // routed rows: 2^-sigma of the row's token
+    __shared__ float xfac[TOK];                                 // routed rows: 2^(sigma/2), undoes the x16 prescale
     __shared__ uint4 tiles[2][TOK * 32];
     __shared__ __attribute__((aligned(16))) _Float16 hsum[2][TOK][16];
     Item it;
@@ -608,7 +613,9 @@ __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
         if (!it.shared) {
             const int tok = a.perm[it.p0 + m] / a.k;
             s = reinterpret_cast<const uint16_t *>(g.x16) + (int64_t)tok * H;
-            hfac[tid] = ldexpf(1.f, -a.hsig[tok]);
+            const int sig = a.hsig[tok];
+            hfac[tid] = ldexpf(1.f, -sig);
+            xfac[tid] = ldexpf(1.f, sig / 2);
         } else {
             s = static_cast<const uint16_t *>(a.x) + (int64_t)(it.p0 + m) * H;
         }
@@ -639,7 +646,8 @@ __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
             for (int tf = 0; tf < 2; ++tf)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
-                    xch[((wv & 3) * TOK + 32 * tf + drow(v, lane)) * 32 + n] = accq[tf][v] * dprev - accm[tf][v] * mprev;
+                    xch[((wv & 3) * TOK + 32 * tf + drow(v, lane)) * 32 + n] =
+                        (accq[tf][v] * dprev - accm[tf][v] * mprev) * xfac[32 * tf + drow(v, lane)];
         }
         __syncthreads();
         if (!up) {
@@ -649,9 +657,10 @@ __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
                 for (int v = 0; v < 16; ++v) {
                     const int tt = 32 * tf + drow(v, lane), d = dst[tt];
                     if (d >= 0)
-                        g.h[(int64_t)d * a.I + r4] = (_Float16)(silu_mul(accq[tf][v] * dprev - accm[tf][v] * mprev,
-                                                                         xch[((wv & 3) * TOK + tt) * 32 + n]) *
-                                                                hfac[tt]);
+                        g.h[(int64_t)d * a.I + r4] =
+                            (_Float16)(silu_mul((accq[tf][v] * dprev - accm[tf][v] * mprev) * xfac[tt],
+                                                xch[((wv & 3) * TOK + tt) * 32 + n]) *
+                                       hfac[tt]);
                 }
         }
     } else if (!it.shared) {
@@ -665,8 +674,9 @@ __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
             for (int v = 0; v < 16; ++v) {
                 const int tt = 32 * tf + drow(v, lane), d = dst[tt];
                 if (d >= 0)
-                    g.h[(int64_t)d * a.I + row] =
-                        (_Float16)(silu_mul(acc[tf][0][v] * dprev[0], acc[tf][1][v] * dprev[1]) * hfac[tt]);
+                    g.h[(int64_t)d * a.I + row] = (_Float16)(silu_mul(acc[tf][0][v] * dprev[0] * xfac[tt],
+                                                                      acc[tf][1][v] * dprev[1] * xfac[tt]) *
+                                                             hfac[tt]);
             }
     } else {
         if (two) sg_loop<true>(a, row, hh, n, src, tiles, acc);
@@ -934,8 +944,9 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
     }
 }
 
-// x (bf16) -> fp16 copy, one workgroup per token row, 8 elements per thread and step; also the exponent of
-// the token's routed h scale (from the row's largest |x|) into hsig[token]
+// x (bf16) -> fp16 copy, one workgroup per token row, 8 elements per thread and step: the row's largest |x|
+// first, then x * 2^-e with e = sigma / 2, where sigma (the exponent of the token's routed h scale, written to
+// hsig[token]) is 2 * (ilogb(max |x|) - 1) clamped to [-100, 100]
 __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t *__restrict__ x, _Float16 *__restrict__ y, int H,
                                                   int32_t *__restrict__ hsig) {
     __shared__ float wmax[4];
@@ -945,20 +956,26 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t *__restrict__ x
     float mx = 0.f;
     for (int i = threadIdx.x; i < n8; i += 256) {
         const uint4 v = xr[i];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        f16x8_t o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            o[2 * j] = (_Float16)__uint_as_float(w[j] << 16);
-            o[2 * j + 1] = (_Float16)__uint_as_float(w[j] & 0xFFFF0000u);
-            mx = fmaxf(mx, bf16x2_absmax(w[j]));
-        }
-        yr[i] = o;
+        mx = fmaxf(fmaxf(mx, fmaxf(bf16x2_absmax(v.x), bf16x2_absmax(v.y))),
+                   fmaxf(bf16x2_absmax(v.z), bf16x2_absmax(v.w)));
     }
     mx = wave_max_f32(mx);
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
     __syncthreads();
-    if (threadIdx.x == 0) hsig[t] = h_sigma(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+    const int sig = h_sigma(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+    if (threadIdx.x == 0) hsig[t] = sig;
+    const int sh = -(sig / 2);
+    for (int i = threadIdx.x; i < n8; i += 256) {
+        const uint4 v = xr[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        f16x8_t o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            o[2 * j] = (_Float16)ldexpf(__uint_as_float(w[j] << 16), sh);
+            o[2 * j + 1] = (_Float16)ldexpf(__uint_as_float(w[j] & 0xFFFF0000u), sh);
+        }
+        yr[i] = o;
+    }
 }
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }

@@ -65,4 +65,7 @@ hipError_t launch_combine(const float *slot_out, const float *topk_w, const floa
 hipError_t launch_combine_steer(const float *slot_out, const float *topk_w, const float *shared_out, int T, int k,
                                 int H, const float *v, float F, float *y, hipStream_t st);
 
+// probe.hip: streaming-read ceiling (measurement only)
+hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink, int n_blocks, hipStream_t st);
+
 }  // namespace moe

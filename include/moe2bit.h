@@ -175,14 +175,17 @@ size_t moe_expert_ffn_workspace(const moe_layer_desc *L, int32_t n_tokens);
  * SwiGLU output h of routed slots is kept in fp16 (decode kernels: T <= 4, or
  * T <= 8 for iq2x gate/up with q2k down and T*k <= 64; grouped-GEMM kernels
  * above that) or fp32 (generic kernels); the shared expert's
- * h in fp32 (decode, generic) or as a bf16 hi + lo pair (grouped GEMM).  The
- * grouped-GEMM kernels read x as fp16 (exact for bf16 values in fp16 range).
- * Range: the fp16 h of token t is stored as h * 2^-s(t), where s(t) =
- * 2 * (ilogb(max_c |x[t][c]|) - 1), clamped to [-100, 100] (0 for an all-zero
- * row), and the down projection multiplies its sums by 2^s(t).  A power of two
- * scales exactly, and h grows as |x|^2, so the stored h stays near unit scale
- * for any input range; the tests cover x scaled by 2^-10 .. 2^12 around unit
- * RMS.  Non-finite inputs give non-finite outputs.
+ * h in fp32 (decode, generic) or as a bf16 hi + lo pair (grouped GEMM).
+ * Range: with s(t) = 2 * (ilogb(max_c |x[t][c]|) - 1), clamped to [-100, 100]
+ * (0 for an all-zero row), the fp16 h of token t is stored as h * 2^-s(t) and
+ * the down projection multiplies its sums by 2^s(t); the grouped-GEMM kernels
+ * read x as fp16 after the same kind of prescale, x * 2^-s(t)/2 (the row's
+ * largest magnitude then lies in [2, 4)), and multiply the gate and up sums by
+ * 2^s(t)/2.  Powers of two scale exactly, so the results do not depend on the
+ * input scale for rows whose largest |x| lies between 2^-48 and 2^48 (beyond
+ * that the clamp lets fp16 h or x over- or underflow); the tests cover x scaled
+ * by 2^-20 .. 2^16 around unit RMS.  Non-finite inputs give non-finite
+ * outputs.
  */
 moe_status moe_expert_ffn(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
                           const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
@@ -241,6 +244,16 @@ moe_status moe_combine(const float *slot_out, const float *topk_w, const float *
 moe_status moe_combine_steer(const float *slot_out, const float *topk_w, const float *shared_out, int32_t n_tokens,
                              int32_t top_k, int32_t hidden, const float *steer_v, float steer_f, float *y,
                              void *stream);
+
+/*
+ * Measurement helper, not part of the layer: reads `bytes` bytes of `buf`
+ * (device, 16-byte aligned, a multiple of 16) once with 16-byte lane loads
+ * in n_blocks workgroups of 256 threads, and XORs each workgroup's fold of the
+ * words into sink[workgroup] (device, n_blocks uint32, contents meaningless).
+ * Timing it gives the sustained HBM read rate at a given byte count, the
+ * measured ceiling the layer's bandwidth-bound kernels are compared with.
+ */
+moe_status moe_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t n_blocks, void *stream);
 
 #ifdef __cplusplus
 }

@@ -74,6 +74,17 @@ def lib():
     return _lib
 
 
+def set_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP loops (the process-wide OpenMP runtime the library links)."""
+    lib()
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
+def get_threads() -> int:
+    lib()
+    return int(ctypes.CDLL("libgomp.so.1").omp_get_max_threads())
+
+
 def _p(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 

@@ -172,3 +172,52 @@ def test_plain_c_consumer(tmp_path):
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert out.returncode == 0 and out.stdout.strip().endswith("ok"), out.stdout + out.stderr
+
+
+def test_binding_rejects_undersized_tensors():
+    """The binding checks every tensor's size against T, k, E and H on the host before a pointer reaches the
+    library (an undersized output would be written out of bounds); host tensors are enough to see the check."""
+    torch = pytest.importorskip("torch")
+    import bit_quantized_moe_permute_amd as m
+    from bit_quantized_moe_permute_amd import LayerDesc
+    i32 = dict(dtype=torch.int32)
+    T, H, E, k = 3, 256, 8, 2
+    x = torch.zeros(T, H, dtype=torch.bfloat16)
+    w = torch.zeros(E, H, dtype=torch.bfloat16)
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    good = dict(topk_idx=torch.zeros(T * k, **i32), topk_w=torch.zeros(T * k), expert_offsets=torch.zeros(E + 1, **i32),
+                perm=torch.zeros(T * k, **i32), active=torch.zeros(E + 1, **i32))
+    for name, short in (("topk_idx", torch.zeros(T * k - 1, **i32)), ("topk_w", torch.zeros(1)),
+                        ("expert_offsets", torch.zeros(E, **i32)), ("perm", torch.zeros(T, **i32)),
+                        ("active", torch.zeros(E, **i32))):
+        args = dict(good, **{name: short})
+        with pytest.raises(ValueError, match=name):
+            m.moe_route(x, w, E, k, args["topk_idx"], args["topk_w"], args["expert_offsets"], args["perm"],
+                        args["active"], ws)
+    with pytest.raises(ValueError, match="w_router"):
+        m.moe_route(x, torch.zeros(E, H + 64, dtype=torch.bfloat16), E, k, *good.values(), ws)
+    with pytest.raises(ValueError, match="tokens"):
+        m.moe_route(x.reshape(-1), w, E, k, *good.values(), ws)
+    with pytest.raises(ValueError, match="logits"):
+        m.moe_route(x, w, E, k, *good.values(), ws, logits=torch.zeros(T, E - 1))
+    d = LayerDesc(hidden=H, inter=128, n_experts=E, top_k=k, shared_inter=128)
+    slot = torch.zeros(T * k, H)
+    shared = torch.zeros(T, H)
+    routing = (good["topk_idx"], good["expert_offsets"], good["perm"], good["active"])
+    with pytest.raises(ValueError, match="slot_out"):
+        m.moe_expert_ffn(d, x, *routing, slot[:-1], shared, ws)
+    with pytest.raises(ValueError, match="shared_out"):
+        m.moe_expert_ffn(d, x, *routing, slot, shared[:-1], ws)
+    with pytest.raises(ValueError, match="hidden"):
+        m.moe_expert_ffn(d, torch.zeros(T, H + 8, dtype=torch.bfloat16), *routing, slot, shared, ws)
+    with pytest.raises(ValueError, match="perm"):
+        m.moe_expert_gate_up(d, x, good["topk_idx"], good["expert_offsets"], good["perm"][:-1], good["active"], ws)
+    with pytest.raises(ValueError, match="y"):
+        m.moe_combine(slot, good["topk_w"], shared, T, k, H, torch.zeros(T, H - 1))
+    with pytest.raises(ValueError, match="steer_v"):
+        m.moe_combine_steer(slot, good["topk_w"], shared, T, k, H, torch.zeros(H - 1), 1.0, torch.zeros(T, H))
+    with pytest.raises(ValueError, match="out"):
+        m.moe_dequantize(2, torch.zeros(84 * 4, dtype=torch.uint8), 1, 4, 256, 0, 1, None, torch.zeros(1023))
+    with pytest.raises(ValueError, match="prepared"):
+        m.moe_prepare_weights(2, 1, 4, 256, torch.zeros(84 * 4, dtype=torch.uint8),
+                              torch.zeros(84 * 4 - 1, dtype=torch.uint8))
