@@ -24,7 +24,7 @@ ABI_VERSION = 2
 EXPORTS = [
     "moe_abi_version", "moe_last_error", "moe_weight_bytes", "moe_prepare_weights", "moe_dequantize",
     "moe_route_workspace", "moe_route", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_expert_gate_up",
-    "moe_expert_down", "moe_combine", "moe_combine_steer", "moe_probe_stream_read",
+    "moe_expert_down", "moe_combine", "moe_combine_steer", "moe_probe_stream_read", "moe_expert_ffn_noalloc",
 ]
 
 
@@ -79,6 +79,8 @@ def _load():
     L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
     L.moe_combine_steer.restype = ctypes.c_int
     L.moe_combine_steer.argtypes = [vp, vp, vp, i32, i32, i32, vp, ctypes.c_float, vp, vp]
+    L.moe_expert_ffn_noalloc.restype = ctypes.c_int
+    L.moe_expert_ffn_noalloc.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.moe_probe_stream_read.restype = ctypes.c_int
     L.moe_probe_stream_read.argtypes = [vp, sz, vp, i32, vp]
     if L.moe_abi_version() != ABI_VERSION:
@@ -230,6 +232,15 @@ def moe_expert_ffn(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, s
     _check(lib.moe_expert_ffn(ctypes.byref(desc), _ptr(x), _dt(x), T, _i32(topk_idx), _i32(expert_offsets),
                               _i32(perm), _i32(active), _f32(slot_out), _f32(shared_out), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_expert_ffn_noalloc(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, slot_out, shared_out,
+                           stream=None):
+    """moe_expert_ffn with the library's static device scratch instead of a workspace (no allocation)."""
+    T = _routing_sizes(desc, x, topk_idx, expert_offsets, perm, active)
+    _output_sizes(desc, T, slot_out, shared_out)
+    _check(lib.moe_expert_ffn_noalloc(ctypes.byref(desc), _ptr(x), _dt(x), T, _i32(topk_idx), _i32(expert_offsets),
+                                      _i32(perm), _i32(active), _f32(slot_out), _f32(shared_out), _stream(stream)))
 
 
 def moe_expert_gate_up(desc: LayerDesc, x, topk_idx, expert_offsets, perm, active, ws, stream=None):

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe2bit.h"
 #include "internal.h"
@@ -208,20 +209,65 @@ size_t moe_expert_ffn_workspace(const moe_layer_desc *L, int32_t n_tokens) {
     return m;
 }
 
+// ---------------------------------------------------------------------------
+// Static device scratch of moe_expert_ffn_noalloc: one copy per GPU, held until
+// the process ends.  In host code `scratch` only names the symbol; its device
+// address is looked up per device with hipGetSymbolAddress and used instead.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's `scratch`, looked up on the first call on that device (with the device
+// current).  The caller's stream must belong to the current device.
+moe_status scratch_for(void *stream, const char *fn, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", fn, dev, kMaxDevices);
+    if (stream) {
+        int sdev = -1;
+        e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+        if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "%s: hipStreamGetDevice: %s", fn, hipGetErrorString(e));
+        if (sdev != dev)
+            return fail(MOE_ERR_INVALID_ARG, "%s: the stream belongs to device %d, the current device is %d", fn,
+                        sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MOE_ERR_DEVICE, "%s: hipGetSymbolAddress of the static scratch: %s", fn,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+// ws == nullptr with static_ws: the kernels' scratch is this device's static `scratch`.
 static moe_status expert_call(const char *fn, int stages, const moe_layer_desc *L, const void *x, int32_t x_dt,
                               int32_t n_tokens, const int32_t *topk_idx, const int32_t *expert_offsets,
                               const int32_t *perm, const int32_t *active, float *slot_out, float *shared_out,
-                              void *ws, size_t ws_bytes, void *stream) {
+                              void *ws, size_t ws_bytes, void *stream, bool static_ws = false) {
     moe_status st = check_layer(L, fn);
     if (st != MOE_OK) return st;
-    if (!x || !topk_idx || !expert_offsets || !perm || !active || !ws)
+    if (!x || !topk_idx || !expert_offsets || !perm || !active || (!ws && !static_ws))
         return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
     if ((stages & moe::STAGE_DOWN) && !slot_out) return fail(MOE_ERR_INVALID_ARG, "%s: null slot_out", fn);
     if (x_dt != MOE_DT_F32 && x_dt != MOE_DT_BF16) return fail(MOE_ERR_INVALID_ARG, "%s: unknown dtype", fn);
     if (n_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "%s: n_tokens < 1", fn);
     if ((stages & moe::STAGE_DOWN) && (L->shared_inter > 0) != (shared_out != nullptr))
         return fail(MOE_ERR_INVALID_ARG, "%s: shared_out must be given iff the layer has a shared expert", fn);
-    if (!aligned(x, 16) || (slot_out && !aligned(slot_out, 16)) || !aligned(ws, 256) ||
+    if (!aligned(x, 16) || (slot_out && !aligned(slot_out, 16)) || (ws && !aligned(ws, 256)) ||
         (shared_out && !aligned(shared_out, 16)))
         return fail(MOE_ERR_INVALID_ARG, "%s: misaligned pointer (x/outputs 16 B, ws 256 B)", fn);
     moe::FfnArgs a = make_args(L, x, x_dt, n_tokens);
@@ -236,7 +282,15 @@ static moe_status expert_call(const char *fn, int stages, const moe_layer_desc *
         return fail(MOE_ERR_UNSUPPORTED, "%s: grouped-GEMM kernels need bf16 x and hidden, inter, "
                                          "shared_inter multiples of 256", fn);
     const size_t need = workspace_for(path, L, n_tokens);
-    if (ws_bytes < need) return fail(MOE_ERR_INVALID_ARG, "%s: workspace too small (%zu < %zu)", fn, ws_bytes, need);
+    if (static_ws) {
+        if (need > MOE_NOALLOC_SCRATCH_BYTES)
+            return fail(MOE_ERR_INVALID_ARG, "%s: %d tokens need %zu bytes of scratch, the static scratch holds %zu; "
+                                             "use moe_expert_ffn with a workspace", fn, n_tokens, need,
+                        (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+        if ((st = scratch_for(stream, fn, &a.ws)) != MOE_OK) return st;
+    } else if (ws_bytes < need) {
+        return fail(MOE_ERR_INVALID_ARG, "%s: workspace too small (%zu < %zu)", fn, ws_bytes, need);
+    }
     hipError_t e;
     if (path == MOE_PATH_GEMV) e = moe::launch_ffn_gemv(a, (hipStream_t)stream);
     else if (path == MOE_PATH_GEMM) e = moe::launch_ffn_gemm(a, (hipStream_t)stream);
@@ -250,6 +304,13 @@ moe_status moe_expert_ffn(const moe_layer_desc *L, const void *x, int32_t x_dt, 
                           void *stream) {
     return expert_call("moe_expert_ffn", moe::STAGE_GATE_UP | moe::STAGE_DOWN, L, x, x_dt, n_tokens, topk_idx,
                        expert_offsets, perm, active, slot_out, shared_out, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_ffn_noalloc(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
+                                  const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
+                                  const int32_t *active, float *slot_out, float *shared_out, void *stream) {
+    return expert_call("moe_expert_ffn_noalloc", moe::STAGE_GATE_UP | moe::STAGE_DOWN, L, x, x_dt, n_tokens,
+                       topk_idx, expert_offsets, perm, active, slot_out, shared_out, nullptr, 0, stream, true);
 }
 
 moe_status moe_expert_gate_up(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,

@@ -192,6 +192,32 @@ moe_status moe_expert_ffn(const moe_layer_desc *L, const void *x, int32_t x_dt, 
                           const int32_t *active, float *slot_out, float *shared_out, void *ws, size_t ws_bytes,
                           void *stream);
 
+/* Bytes of the static device scratch moe_expert_ffn_noalloc uses (one copy per
+ * GPU the library runs on, held until the process ends). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * moe_expert_ffn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments and kernels without `ws` -- their scratch (h, its
+ * per-token scale exponents, the fp16 copy of x, the shared expert's h) lives
+ * in a static device array of MOE_NOALLOC_SCRATCH_BYTES bytes, one per GPU.
+ * Results are bit-identical to moe_expert_ffn's.  The call allocates nothing;
+ * the first call on a device looks the array's address up (with that device
+ * current).  Nothing in the array must start at zero, and it keeps the last
+ * call's contents.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (several streams or threads) race and give
+ * wrong results: serialize them on one stream.  Returns MOE_ERR_INVALID_ARG,
+ * launching nothing, when the chosen kernel family needs more scratch than the
+ * array holds -- decode and verify calls (up to 8 tokens) need at most 330 KB
+ * at hidden 4096, intermediate 2048, top-8; the grouped-GEMM kernels about
+ * 48 KiB per token at that shape, so up to about 340 tokens -- or when `stream`
+ * belongs to another device than the current one.
+ */
+moe_status moe_expert_ffn_noalloc(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
+                                  const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
+                                  const int32_t *active, float *slot_out, float *shared_out, void *stream);
+
 /*
  * The two halves of moe_expert_ffn, for callers that schedule them apart (or
  * time them): moe_expert_gate_up writes the SwiGLU activations h of every slot
