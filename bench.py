@@ -231,7 +231,7 @@ def decode_bytes(H, I, E, k, Is):
 def stream_read_peak(nbytes, reps=200):
     """Measured streaming-read rate (GB/s) of the library's plain read kernel at `nbytes` per launch: reps
     launches over distinct, consecutive windows of a 4 GiB buffer (so no launch finds its bytes in the 256 MB
-    last-level cache), best of three grid sizes."""
+    last-level cache), best of five grid sizes."""
     import torch
     from bit_quantized_moe_permute_amd import moe_probe_stream_read
     span = 4 << 30
@@ -239,7 +239,7 @@ def stream_read_peak(nbytes, reps=200):
     buf = torch.empty(span, dtype=torch.uint8, device="cuda")
     buf.fill_(3)
     best = None
-    for blocks in (1024, 2048, 4096):
+    for blocks in (1024, 2048, 4096, 8192, 16384):
         sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
         n_win = span // nbytes
 
@@ -302,7 +302,7 @@ def main():
 
     import synth
     from bit_quantized_moe_permute_amd import moe_combine, moe_expert_down, moe_expert_gate_up, moe_route
-    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward, forward_layer
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -326,7 +326,7 @@ def main():
 
     def step(i):
         b = bufs[i % 2]
-        forward(layers[i % args.layers], x[i % n_tok: i % n_tok + 1], b)
+        forward_layer(layers[i % args.layers], x[i % n_tok: i % n_tok + 1], b)
         return b.y
 
     log(f"decode: warmup {W} steps, {K} steps captured in a HIP graph")
@@ -335,10 +335,20 @@ def main():
     value = K / wall
     log(f"{K} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms -> {value:.0f} tokens/s")
 
+    # the same steps as the three calls moe_route, moe_expert_ffn, moe_combine (routing in two launches)
+    def step3(i):
+        b = bufs[i % 2]
+        forward(layers[i % args.layers], x[i % n_tok: i % n_tok + 1], b)
+        return b.y
+
+    twall, _ = graph_steps(step3, K, W)
+    three_calls = {"tokens_per_s": round(K / twall, 1), "ms_per_step": round(twall * 1e3 / K, 5)}
+    log(f"decode as three calls: {K / twall:.0f} tokens/s")
+
     # the same decode steps on one layer copy (consecutive tokens may find experts in the 256 MB last-level cache)
     def step1(i):
         b = bufs[i % 2]
-        forward(layers[0], x[i % n_tok: i % n_tok + 1], b)
+        forward_layer(layers[0], x[i % n_tok: i % n_tok + 1], b)
         return b.y
 
     nwall, _ = graph_steps(step1, K, W)
@@ -353,7 +363,7 @@ def main():
 
     def vstep(i):
         b = vbufs[i % 2]
-        forward(layers[i % args.layers], vx[3 * i: 3 * i + 3], b)
+        forward_layer(layers[i % args.layers], vx[3 * i: 3 * i + 3], b)
         return b.y
 
     vwall, _ = graph_steps(vstep, vK, min(W, vK))
@@ -369,7 +379,7 @@ def main():
 
         def mstep(i, M=M, mx=mx, mbufs=mbufs):
             b = mbufs[i % 2]
-            forward(layers[i % args.layers], mx[M * i: M * i + M], b)
+            forward_layer(layers[i % args.layers], mx[M * i: M * i + M], b)
             return b.y
 
         mwall, _ = graph_steps(mstep, vK, min(W, vK))
@@ -478,7 +488,7 @@ def main():
 
         def qstep(i):
             b = bufs[i % 2]
-            forward(layers4[i % n4], x[i % n_tok: i % n_tok + 1], b)
+            forward_layer(layers4[i % n4], x[i % n_tok: i % n_tok + 1], b)
             return b.y
 
         qwall, _ = graph_steps(qstep, K, W)
@@ -508,6 +518,7 @@ def main():
         "step": {"bytes_per_token": nbytes["total"], "effective_GBps": round(step_bw, 1),
                  "hbm_frac": round(step_bw / HBM_PEAK_GBS, 4), "graph_gpu_ms": round(gpu_ms, 3)},
         "decode_kernels": decode_kernels,
+        "decode_three_calls": three_calls,
         "verify": verify,
         "decode_steer": steer,
         "decode_no_cycling": no_cycling,
@@ -521,7 +532,7 @@ def collect(DL, xd, T):
     """Layer outputs of consecutive T-token calls over all rows of xd (device bf16 [N][H]) on layer DL: routing,
     weights, slot, shared and layer outputs as host arrays."""
     import torch
-    from bit_quantized_moe_permute_amd.layer import LayerBuffers, forward
+    from bit_quantized_moe_permute_amd.layer import LayerBuffers, forward_layer
     N, H = xd.shape
     steps = N // T
     b = LayerBuffers.allocate(DL, T)
@@ -532,7 +543,7 @@ def collect(DL, xd, T):
     tw = torch.empty(steps * T, DL.k, dtype=torch.float32, device=xd.device)
     for s in range(steps):
         r = slice(s * T, (s + 1) * T)
-        forward(DL, xd[r], b)
+        forward_layer(DL, xd[r], b)
         y[r].copy_(b.y)
         slot[s * T * DL.k: (s + 1) * T * DL.k].copy_(b.slot_out)
         sh[r].copy_(b.shared_out)
@@ -585,7 +596,7 @@ def prefill_bench(L, DL, reps, names, samples=None):
 
     import synth
     from bit_quantized_moe_permute_amd import moe_expert_down, moe_expert_gate_up
-    from bit_quantized_moe_permute_amd.layer import LayerBuffers, forward
+    from bit_quantized_moe_permute_amd.layer import LayerBuffers, forward_layer
 
     sp = L.spec
     H, I, k, Is = sp.hidden, sp.inter, sp.top_k, sp.shared_inter
@@ -603,7 +614,7 @@ def prefill_bench(L, DL, reps, names, samples=None):
 
         def prompt():
             for c0, n in chunks:
-                forward(DL, xd[c0:c0 + n], bufs[n])
+                forward_layer(DL, xd[c0:c0 + n], bufs[n])
 
         prompt()
         torch.cuda.synchronize()
@@ -618,7 +629,7 @@ def prefill_bench(L, DL, reps, names, samples=None):
         # gate/up and down stages alone, on the first (largest) chunk
         c0, n = chunks[0]
         b = bufs[n]
-        forward(DL, xd[c0:c0 + n], b)
+        forward_layer(DL, xd[c0:c0 + n], b)
         torch.cuda.synchronize()
         xc = xd[c0:c0 + n]
         gu_us = graph_time_us(lambda i: moe_expert_gate_up(DL.desc, xc, b.topk_idx, b.offsets, b.perm, b.active,
@@ -649,7 +660,7 @@ def prefill_bench(L, DL, reps, names, samples=None):
             rows_all = []
             for ci, (c0, n) in enumerate(chunks):
                 bb = bufs[n]
-                forward(DL, xd[c0:c0 + n], bb)
+                forward_layer(DL, xd[c0:c0 + n], bb)
                 torch.cuda.synchronize()
                 idx = bb.topk_idx.cpu().numpy()
                 full = name == "prefill" or (name == "long" and ci == 0)

@@ -25,6 +25,7 @@ EXPORTS = [
     "moe_abi_version", "moe_last_error", "moe_weight_bytes", "moe_prepare_weights", "moe_dequantize",
     "moe_route_workspace", "moe_route", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_expert_gate_up",
     "moe_expert_down", "moe_combine", "moe_combine_steer", "moe_probe_stream_read", "moe_expert_ffn_noalloc",
+    "moe_layer_workspace", "moe_layer",
 ]
 
 
@@ -81,6 +82,11 @@ def _load():
     L.moe_combine_steer.argtypes = [vp, vp, vp, i32, i32, i32, vp, ctypes.c_float, vp, vp]
     L.moe_expert_ffn_noalloc.restype = ctypes.c_int
     L.moe_expert_ffn_noalloc.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_layer_workspace.restype = sz
+    L.moe_layer_workspace.argtypes = [ctypes.POINTER(LayerDesc), i32]
+    L.moe_layer.restype = ctypes.c_int
+    L.moe_layer.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                            ctypes.c_float, vp, vp, sz, vp]
     L.moe_probe_stream_read.restype = ctypes.c_int
     L.moe_probe_stream_read.argtypes = [vp, sz, vp, i32, vp]
     if L.moe_abi_version() != ABI_VERSION:
@@ -276,6 +282,28 @@ def moe_combine_steer(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, ste
     _need(steer_v, hidden, "steer_v")
     _check(lib.moe_combine_steer(_f32(slot_out), _f32(topk_w), _f32(shared_out), n_tokens, top_k, hidden,
                                  _f32(steer_v), float(steer_f), _f32(y), _stream(stream)))
+
+
+def moe_layer_workspace(desc: LayerDesc, n_tokens: int) -> int:
+    return lib.moe_layer_workspace(ctypes.byref(desc), n_tokens)
+
+
+def moe_layer(desc: LayerDesc, x, w_router, topk_idx, topk_w, expert_offsets, perm, active, slot_out, shared_out, y,
+              ws, bias=None, logits=None, steer_v=None, steer_f=0.0, stream=None):
+    """route -> expert FFN -> combine (+ steering when steer_v is given) in one C-ABI call."""
+    T = _routing_sizes(desc, x, topk_idx, expert_offsets, perm, active)
+    if w_router.dim() != 2 or tuple(w_router.shape) != (desc.n_experts, desc.hidden):
+        raise ValueError(f"w_router must be [{desc.n_experts}][{desc.hidden}], got shape {tuple(w_router.shape)}")
+    _output_sizes(desc, T, slot_out, shared_out)
+    _need(topk_w, T * desc.top_k, "topk_w")
+    _need(bias, desc.n_experts, "bias")
+    _need(logits, T * desc.n_experts, "logits")
+    _need(steer_v, desc.hidden, "steer_v")
+    _need(y, T * desc.hidden, "y")
+    _check(lib.moe_layer(ctypes.byref(desc), _ptr(x), _dt(x), T, _ptr(w_router), _dt(w_router), _f32(bias),
+                         _i32(topk_idx), _f32(topk_w), _f32(logits), _i32(expert_offsets), _i32(perm), _i32(active),
+                         _f32(slot_out), _f32(shared_out), _f32(steer_v), float(steer_f), _f32(y), _ptr(ws),
+                         ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_probe_stream_read(buf, nbytes, sink, n_blocks, stream=None):

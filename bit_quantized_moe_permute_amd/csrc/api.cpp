@@ -107,30 +107,41 @@ size_t moe_route_workspace(int32_t n_tokens, int32_t n_experts, int32_t top_k) {
     return ((size_t)n_tokens * n_experts * sizeof(float) + 255) / 256 * 256;
 }
 
-moe_status moe_route(const void *x, int32_t x_dt, int32_t n_tokens, int32_t hidden, const void *w_router,
-                     int32_t w_dt, int32_t n_experts, const float *bias, int32_t top_k, int32_t *topk_idx,
-                     float *topk_w, float *logits, int32_t *expert_offsets, int32_t *perm, int32_t *active, void *ws,
-                     size_t ws_bytes, void *stream) {
+// Host checks of the routing arguments; fills `a` (logits scratch at ws).
+static moe_status route_args(const char *fn, const void *x, int32_t x_dt, int32_t n_tokens, int32_t hidden,
+                             const void *w_router, int32_t w_dt, int32_t n_experts, const float *bias, int32_t top_k,
+                             int32_t *topk_idx, float *topk_w, float *logits, int32_t *expert_offsets, int32_t *perm,
+                             int32_t *active, void *ws, size_t ws_bytes, moe::RouteArgs &a) {
     if (!x || !w_router || !topk_idx || !topk_w || !expert_offsets || !perm || !active || !ws)
-        return fail(MOE_ERR_INVALID_ARG, "moe_route: null pointer");
+        return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
     if ((x_dt != MOE_DT_F32 && x_dt != MOE_DT_BF16) || (w_dt != MOE_DT_F32 && w_dt != MOE_DT_BF16))
-        return fail(MOE_ERR_INVALID_ARG, "moe_route: unknown dtype");
-    if (n_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "moe_route: n_tokens < 1");
-    if (hidden < 64 || hidden % 64) return fail(MOE_ERR_INVALID_ARG, "moe_route: hidden %% 64 != 0");
-    if (n_experts < 1 || n_experts > 256) return fail(MOE_ERR_INVALID_ARG, "moe_route: n_experts outside [1, 256]");
-    if (top_k < 1 || top_k > n_experts) return fail(MOE_ERR_INVALID_ARG, "moe_route: top_k outside [1, n_experts]");
-    if ((int64_t)n_tokens * top_k > (int64_t)1 << 30) return fail(MOE_ERR_INVALID_ARG, "moe_route: too many slots");
+        return fail(MOE_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+    if (n_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "%s: n_tokens < 1", fn);
+    if (hidden < 64 || hidden % 64) return fail(MOE_ERR_INVALID_ARG, "%s: hidden %% 64 != 0", fn);
+    if (n_experts < 1 || n_experts > 256) return fail(MOE_ERR_INVALID_ARG, "%s: n_experts outside [1, 256]", fn);
+    if (top_k < 1 || top_k > n_experts) return fail(MOE_ERR_INVALID_ARG, "%s: top_k outside [1, n_experts]", fn);
+    if ((int64_t)n_tokens * top_k > (int64_t)1 << 30) return fail(MOE_ERR_INVALID_ARG, "%s: too many slots", fn);
     if (ws_bytes < moe_route_workspace(n_tokens, n_experts, top_k))
-        return fail(MOE_ERR_INVALID_ARG, "moe_route: workspace too small (%zu < %zu)", ws_bytes,
+        return fail(MOE_ERR_INVALID_ARG, "%s: workspace too small (%zu < %zu)", fn, ws_bytes,
                     moe_route_workspace(n_tokens, n_experts, top_k));
     if (!aligned(ws, 16) || !aligned(x, 4) || !aligned(w_router, 4))
-        return fail(MOE_ERR_INVALID_ARG, "moe_route: misaligned pointer");
-    moe::RouteArgs a;
+        return fail(MOE_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
     a.x = x; a.x_bf16 = x_dt == MOE_DT_BF16; a.T = n_tokens; a.H = hidden;
     a.w = w_router; a.w_bf16 = w_dt == MOE_DT_BF16; a.E = n_experts; a.bias = bias; a.k = top_k;
     a.topk_idx = topk_idx; a.topk_w = topk_w; a.logits_out = logits;
     a.offsets = expert_offsets; a.perm = perm; a.active = active;
     a.logits_ws = static_cast<float *>(ws);
+    return MOE_OK;
+}
+
+moe_status moe_route(const void *x, int32_t x_dt, int32_t n_tokens, int32_t hidden, const void *w_router,
+                     int32_t w_dt, int32_t n_experts, const float *bias, int32_t top_k, int32_t *topk_idx,
+                     float *topk_w, float *logits, int32_t *expert_offsets, int32_t *perm, int32_t *active, void *ws,
+                     size_t ws_bytes, void *stream) {
+    moe::RouteArgs a;
+    moe_status st = route_args("moe_route", x, x_dt, n_tokens, hidden, w_router, w_dt, n_experts, bias, top_k,
+                               topk_idx, topk_w, logits, expert_offsets, perm, active, ws, ws_bytes, a);
+    if (st != MOE_OK) return st;
     return from_hip(moe::launch_route(a, (hipStream_t)stream), "moe_route");
 }
 
@@ -253,11 +264,21 @@ moe_status scratch_for(void *stream, const char *fn, void **out) {
 
 }  // namespace
 
+// Routing done inside the gate/up launch of a one-token call (moe_layer): the logits to select from and the
+// routing outputs to write.
+struct InKernelRoute {
+    const float *logits;
+    int32_t *idx;
+    float *w;
+    int32_t *offsets, *perm, *active;
+};
+
 // ws == nullptr with static_ws: the kernels' scratch is this device's static `scratch`.
 static moe_status expert_call(const char *fn, int stages, const moe_layer_desc *L, const void *x, int32_t x_dt,
                               int32_t n_tokens, const int32_t *topk_idx, const int32_t *expert_offsets,
                               const int32_t *perm, const int32_t *active, float *slot_out, float *shared_out,
-                              void *ws, size_t ws_bytes, void *stream, bool static_ws = false) {
+                              void *ws, size_t ws_bytes, void *stream, bool static_ws = false,
+                              const InKernelRoute *route = nullptr) {
     moe_status st = check_layer(L, fn);
     if (st != MOE_OK) return st;
     if (!x || !topk_idx || !expert_offsets || !perm || !active || (!ws && !static_ws))
@@ -290,6 +311,11 @@ static moe_status expert_call(const char *fn, int stages, const moe_layer_desc *
         if ((st = scratch_for(stream, fn, &a.ws)) != MOE_OK) return st;
     } else if (ws_bytes < need) {
         return fail(MOE_ERR_INVALID_ARG, "%s: workspace too small (%zu < %zu)", fn, ws_bytes, need);
+    }
+    if (route) {
+        a.sel_logits = route->logits;
+        a.sel_idx = route->idx; a.sel_w = route->w;
+        a.sel_offsets = route->offsets; a.sel_perm = route->perm; a.sel_active = route->active;
     }
     hipError_t e;
     if (path == MOE_PATH_GEMV) e = moe::launch_ffn_gemv(a, (hipStream_t)stream);
@@ -350,6 +376,58 @@ moe_status moe_combine_steer(const float *slot_out, const float *topk_w, const f
     return from_hip(moe::launch_combine_steer(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, steer_v, steer_f,
                                               y, (hipStream_t)stream),
                     "moe_combine_steer");
+}
+
+static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+size_t moe_layer_workspace(const moe_layer_desc *L, int32_t n_tokens) {
+    if (n_tokens < 1 || check_layer(L, "moe_layer_workspace") != MOE_OK) return 0;
+    return align256(moe_route_workspace(n_tokens, L->n_experts, L->top_k)) + moe_expert_ffn_workspace(L, n_tokens);
+}
+
+moe_status moe_layer(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens, const void *w_router,
+                     int32_t w_dt, const float *bias, int32_t *topk_idx, float *topk_w, float *logits,
+                     int32_t *expert_offsets, int32_t *perm, int32_t *active, float *slot_out, float *shared_out,
+                     const float *steer_v, float steer_f, float *y, void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "moe_layer";
+    moe_status st = check_layer(L, fn);
+    if (st != MOE_OK) return st;
+    if (!y || !slot_out) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(y, 4) || (steer_v && !aligned(steer_v, 4)))
+        return fail(MOE_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if (steer_v && !std::isfinite(steer_f)) return fail(MOE_ERR_INVALID_ARG, "%s: steering strength not finite", fn);
+    const size_t rws = align256(moe_route_workspace(n_tokens, L->n_experts, L->top_k));
+    if (!ws || ws_bytes < rws) return fail(MOE_ERR_INVALID_ARG, "%s: workspace too small", fn);
+    moe::RouteArgs ra;
+    st = route_args(fn, x, x_dt, n_tokens, L->hidden, w_router, w_dt, L->n_experts, bias, L->top_k, topk_idx, topk_w,
+                    logits, expert_offsets, perm, active, ws, rws, ra);
+    if (st != MOE_OK) return st;
+    void *fws = static_cast<char *>(ws) + rws;
+    const size_t fbytes = ws_bytes - rws;
+    // one token on the decode kernels: the routed gate/up workgroups select the token's experts from the logits
+    // themselves, so routing takes one launch (the logits) instead of two
+    moe::FfnArgs probe = make_args(L, x, x_dt, n_tokens);
+    const bool in_kernel = n_tokens == 1 && L->top_k <= moe::SEL_MAXK && x_dt == MOE_DT_BF16 &&
+                           choose_path(L, probe) == MOE_PATH_GEMV && moe::ffn_gemv_supported(probe);
+    const hipStream_t hs = (hipStream_t)stream;
+    if (in_kernel) {
+        if ((st = from_hip(moe::launch_route_logits(ra, hs), fn)) != MOE_OK) return st;
+        const InKernelRoute r{ra.logits_ws, topk_idx, topk_w, expert_offsets, perm, active};
+        st = expert_call(fn, moe::STAGE_GATE_UP, L, x, x_dt, n_tokens, topk_idx, expert_offsets, perm, active,
+                         nullptr, nullptr, fws, fbytes, stream, false, &r);
+        if (st != MOE_OK) return st;
+        st = expert_call(fn, moe::STAGE_DOWN, L, x, x_dt, n_tokens, topk_idx, expert_offsets, perm, active, slot_out,
+                         shared_out, fws, fbytes, stream);
+    } else {
+        if ((st = from_hip(moe::launch_route(ra, hs), fn)) != MOE_OK) return st;
+        st = expert_call(fn, moe::STAGE_GATE_UP | moe::STAGE_DOWN, L, x, x_dt, n_tokens, topk_idx, expert_offsets,
+                         perm, active, slot_out, shared_out, fws, fbytes, stream);
+    }
+    if (st != MOE_OK) return st;
+    const int T = n_tokens, k = L->top_k, H = L->hidden;
+    if (steer_v)
+        return from_hip(moe::launch_combine_steer(slot_out, topk_w, shared_out, T, k, H, steer_v, steer_f, y, hs), fn);
+    return from_hip(moe::launch_combine(slot_out, topk_w, shared_out, T, k, H, y, hs), fn);
 }
 
 moe_status moe_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t n_blocks, void *stream) {

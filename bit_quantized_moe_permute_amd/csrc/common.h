@@ -227,3 +227,45 @@ __device__ __forceinline__ float bf16x2_absmax_value(uint32_t acc) {
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Top-k selection keys.  Expert e with logit l has the 64-bit key (orderable
+// bits of l + 0, then 255 - e): a larger key is a larger logit, ties going to
+// the lower index, and keys are distinct.  -0 compares equal to +0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned long long logit_key(float l, int e) {
+    const uint32_t u = __float_as_uint(l + 0.0f);
+    const uint32_t ord = u ^ ((u >> 31) ? 0xFFFFFFFFu : 0x80000000u);
+    return ((unsigned long long)ord << 32) | (uint32_t)(255 - e);
+}
+__device__ __forceinline__ int key_expert(unsigned long long m) { return 255 - (int)(uint32_t)m; }
+
+// max(m, m of the lane that DPP control CTRL reads), 64-bit; every CTRL used here gives every lane a source
+template <int CTRL> __device__ __forceinline__ unsigned long long max_dpp_u64(unsigned long long m) {
+    const int lo = (int)(uint32_t)m, hi = (int)(uint32_t)(m >> 32);
+    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
+    const unsigned long long o = ((unsigned long long)ohi << 32) | olo;
+    return o > m ? o : m;
+}
+
+__device__ __forceinline__ unsigned long long lane_u64(unsigned long long m, int l) {
+    return ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(m >> 32), l) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)m, l);
+}
+
+// Wave-wide maximum of a 64-bit value: within each row of 16 lanes by DPP (quad swaps 1 and 2, half-row
+// mirror, row mirror), then across the four rows from one lane of each.
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long m) {
+    m = max_dpp_u64<0xB1>(m);          // quad_perm [1,0,3,2]
+    m = max_dpp_u64<0x4E>(m);          // quad_perm [2,3,0,1]
+    m = max_dpp_u64<0x141>(m);         // row_half_mirror
+    m = max_dpp_u64<0x140>(m);         // row_mirror
+    const unsigned long long a = lane_u64(m, 0), b = lane_u64(m, 16), c = lane_u64(m, 32), d = lane_u64(m, 48);
+    const unsigned long long ab = a > b ? a : b, cd = c > d ? c : d;
+    return ab > cd ? ab : cd;
+}
+
+}  // namespace moe

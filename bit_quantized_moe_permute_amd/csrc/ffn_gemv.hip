@@ -333,8 +333,88 @@ __device__ void shared_gateup(const FfnArgs &a, const Tokens<MAXM> &tk, int row0
     }
 }
 
+// Expert ai (0 <= ai < k) of a one-token call, in selection order.  With a.sel_logits the calling wave selects
+// the token's experts from its E logits itself (every lane gets the same result): k rounds of a wave-wide maximum
+// of the selection keys, the order moe_route's selection defines.  With `write` the wave also writes the routing
+// outputs of the call: topk_idx, the softmax over the selected logits (binary64, summed in selection order, as
+// moe_route computes it), the expert offsets, the permutation and the active list.  Without a.sel_logits the
+// routing is already in topk_idx.
+__device__ __forceinline__ int one_token_expert(const FfnArgs &a, int ai, bool write) {
+    if (!a.sel_logits) return a.topk_idx[min(ai, a.k - 1)];
+    const int lane = threadIdx.x & 63, E = a.E, k = a.k;
+    write = write && (threadIdx.x >> 6) == 0;                // one wave writes
+    unsigned long long kk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        kk[i] = e < E ? logit_key(a.sel_logits[e], e) : 0ull;
+    }
+    int mine = 0, sel[SEL_MAXK];
+#pragma unroll
+    for (int j = 0; j < SEL_MAXK; ++j) {
+        sel[j] = 0;
+        if (j < k) {
+            const unsigned long long m1 = kk[0] > kk[1] ? kk[0] : kk[1];
+            const unsigned long long m2 = kk[2] > kk[3] ? kk[2] : kk[3];
+            const unsigned long long m = wave_max_u64(m1 > m2 ? m1 : m2);
+            sel[j] = key_expert(m);
+            if (j == ai) mine = sel[j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (kk[i] == m) kk[i] = 0ull;                       // keys are distinct: one owner
+        }
+    }
+    if (write) {
+        double ex[SEL_MAXK], den = 0.0;
+        const double l0 = (double)a.sel_logits[sel[0]];
+#pragma unroll
+        for (int j = 0; j < SEL_MAXK; ++j) {
+            ex[j] = 0.0;
+            if (j < k) {
+                ex[j] = exp((double)a.sel_logits[sel[j]] - l0);
+                den += ex[j];
+            }
+        }
+        // lane j < k: slot j = (token 0, rank j); its place among the selected experts in ascending order
+        int rank = 0, my_e = 0;
+        double my_ex = 0.0;
+#pragma unroll
+        for (int j = 0; j < SEL_MAXK; ++j) {
+            if (j < k && j == lane) { my_e = sel[j]; my_ex = ex[j]; }
+        }
+#pragma unroll
+        for (int j = 0; j < SEL_MAXK; ++j) rank += (j < k && sel[j] < my_e) ? 1 : 0;
+        if (lane < k) {
+            a.sel_idx[lane] = my_e;
+            a.sel_w[lane] = (float)(my_ex / den);
+            a.sel_perm[rank] = lane;
+            a.sel_active[1 + rank] = my_e;
+        }
+        if (lane == 0) a.sel_active[0] = k;
+        for (int e = lane; e <= E; e += 64) {
+            int c = 0;
+#pragma unroll
+            for (int j = 0; j < SEL_MAXK; ++j) c += (j < k && sel[j] < e) ? 1 : 0;
+            a.sel_offsets[e] = c;
+        }
+    }
+    return mine;
+}
+
 template <int MAXM>
-__device__ __forceinline__ bool routed_tokens(const FfnArgs &a, int ai, int &e, Tokens<MAXM> &tk) {
+__device__ __forceinline__ bool routed_tokens(const FfnArgs &a, int ai, int &e, Tokens<MAXM> &tk,
+                                              bool writer = false) {
+    if (a.T == 1) {                              // one token: expert ai in selection order, slot ai
+        if (ai >= a.k) return false;
+        e = one_token_expert(a, ai, writer);
+        tk.n = 1;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            tk.slot[m] = ai;
+            tk.tok[m] = 0;
+        }
+        return true;
+    }
     if (ai >= a.active[0]) return false;
     e = a.active[1 + ai];
     const int o0 = a.offsets[e];
@@ -463,10 +543,11 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
     // requested by every wave (unconditional loads, clamped indices) before
     // any wave requests weights, and the tables and activation pieces are
     // built while the weights stream in.
-    const int n_active = active[0];
-    const int e = min(max(active[1 + ai], 0), a.E - 1);      // in range even for an idle workgroup
+    // one token (MAXM == 1): expert ai in selection order (selected here from the logits when the launch
+    // routes), slot ai; several tokens: the ai-th active expert, slots found by a ballot at the end
+    const int n_active = MAXM == 1 ? a.k : active[0];
     const int n_slots = a.T * a.k;
-    const int sel_raw = a.topk_idx[min(lane, n_slots - 1)];
+    const int sel_raw = MAXM == 1 ? 0 : a.topk_idx[min(lane, n_slots - 1)];
     uint2 cbrow[4];                                          // rows tid + i * blockDim (blockDim >= 64)
 #pragma unroll
     for (int i = 0; i < 4; ++i) cbrow[i] = reinterpret_cast<const uint2 *>(a.codebook)[min(tid + i * (int)blockDim.x, 255)];
@@ -474,6 +555,8 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
 #pragma unroll
     for (int m = 0; m < MAXM; ++m)
         xv[m] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + (int64_t)min(m, a.T - 1) * H + 8 * tid);
+    __builtin_amdgcn_sched_barrier(0);
+    const int e = min(max(MAXM == 1 ? one_token_expert(a, ai, ai == 0 && row0 == 0) : active[1 + ai], 0), a.E - 1);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -597,8 +680,8 @@ __device__ __forceinline__ void routed_gateup_mfma(const FfnArgs &a, const int32
         }
     }
     __syncthreads();
-    // --- token m's slot for this expert: m*k + j where topk_idx[m][j] == e (at most one j)
-    const uint64_t hit = __ballot(sel == e);
+    // --- token m's slot for this expert: m*k + j where topk_idx[m][j] == e (at most one j); one token: slot ai
+    const uint64_t hit = MAXM == 1 ? (1ull << ai) : __ballot(sel == e);
     const uint64_t kmask = a.k >= 64 ? ~0ull : (1ull << a.k) - 1ull;
     for (int i = tid; i < MF_RB * MAXM * 16; i += blockDim.x) {
         const int nn = i & 15, m = (i >> 4) % MAXM, rb = (i >> 4) / MAXM;
@@ -911,7 +994,7 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(FfnArgs a, int wgs_per_expe
         }
         int e;
         Tokens<MAXM> tk;
-        if (!routed_tokens<MAXM>(a, bid / wgs_per_expert, e, tk)) return;
+        if (!routed_tokens<MAXM>(a, bid / wgs_per_expert, e, tk, bid == 0)) return;
         constexpr int ROWS = WAVES * NR * (64 / LPR);
         if constexpr (FG == FMT_Q4K) routed_gateup_q4k<LPR, CPL, MAXM, NR>(a, e, tk, (bid % wgs_per_expert) * ROWS, h);
         else routed_gateup<LPR, CPL, MAXM, NR>(a, e, tk, (bid % wgs_per_expert) * ROWS, cb4, sgn, h);

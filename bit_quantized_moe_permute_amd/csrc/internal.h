@@ -32,6 +32,8 @@ struct RouteArgs {
     float *logits_ws;    // [T][E] scratch
 };
 hipError_t launch_route(const RouteArgs &a, hipStream_t st);
+// the router logits alone (into a.logits_ws, and a.logits_out when set)
+hipError_t launch_route_logits(const RouteArgs &a, hipStream_t st);
 
 // ffn_*.hip
 struct FfnArgs {
@@ -48,7 +50,15 @@ struct FfnArgs {
     int32_t *hsig;                     // [T] exponent of the routed fp16 h per token (workspace; fp16-h kernels)
     void *ws;
     int stages;                        // bit 0: gate/up + SwiGLU, bit 1: down
+    // One-token routing inside the gate/up launch (T == 1, k <= SEL_MAXK): when sel_logits is set, every routed
+    // gate/up workgroup selects the token's experts from these E fp32 logits itself (topk_idx is not read), and
+    // the workgroup of the first selected expert's first rows writes the routing outputs below, as moe_route does.
+    const float *sel_logits;
+    int32_t *sel_idx;
+    float *sel_w;
+    int32_t *sel_offsets, *sel_perm, *sel_active;
 };
+constexpr int SEL_MAXK = 16;
 enum { STAGE_GATE_UP = 1, STAGE_DOWN = 2 };
 size_t ffn_workspace_generic(int H, int I, int E, int k, int Is, int T);
 hipError_t launch_ffn_generic(const FfnArgs &a, hipStream_t st);

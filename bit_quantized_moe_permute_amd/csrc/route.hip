@@ -246,32 +246,6 @@ __global__ __launch_bounds__(256) void k_router_logits_small(const void *__restr
     }
 }
 
-// max(m, m of the lane that DPP control CTRL reads), 64-bit; every CTRL used here gives every lane a source
-template <int CTRL> __device__ __forceinline__ unsigned long long max_dpp(unsigned long long m) {
-    const int lo = (int)(uint32_t)m, hi = (int)(uint32_t)(m >> 32);
-    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
-    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
-    const unsigned long long o = ((unsigned long long)ohi << 32) | olo;
-    return o > m ? o : m;
-}
-
-__device__ __forceinline__ unsigned long long lane_u64(unsigned long long m, int l) {
-    return ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(m >> 32), l) << 32) |
-           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)m, l);
-}
-
-// Wave-wide maximum of a 64-bit value: within each row of 16 lanes by DPP (quad swaps 1 and 2, half-row
-// mirror, row mirror), then across the four rows from one lane of each.
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long m) {
-    m = max_dpp<0xB1>(m);          // quad_perm [1,0,3,2]
-    m = max_dpp<0x4E>(m);          // quad_perm [2,3,0,1]
-    m = max_dpp<0x141>(m);         // row_half_mirror
-    m = max_dpp<0x140>(m);         // row_mirror
-    const unsigned long long a = lane_u64(m, 0), b = lane_u64(m, 16), c = lane_u64(m, 32), d = lane_u64(m, 48);
-    const unsigned long long ab = a > b ? a : b, cd = c > d ? c : d;
-    return ab > cd ? ab : cd;
-}
-
 // Top-k, weights and permutation for T <= 8 tokens in one workgroup of 1024
 // threads.  Expert e of token t carries the key (orderable logit bits, then
 // 255 - e): a larger key is a larger logit, ties going to the lower index, and
@@ -304,9 +278,7 @@ __global__ __launch_bounds__(1024) void k_select_small(const float *__restrict__
         if (q < T) {
             const float l = e < E ? logits[q * E + e] : 0.f;
             lg[q][e] = l;
-            const uint32_t u = __float_as_uint(l + 0.0f);                   // -0 compares equal to +0
-            const uint32_t ord = u ^ ((u >> 31) ? 0xFFFFFFFFu : 0x80000000u);
-            key[q][e] = e < E ? (((unsigned long long)ord << 32) | (uint32_t)(255 - e)) : 0ull;
+            key[q][e] = e < E ? logit_key(l, e) : 0ull;
         }
         __syncthreads();
         for (int t = 0; t < T; ++t) {
@@ -332,15 +304,13 @@ __global__ __launch_bounds__(1024) void k_select_small(const float *__restrict__
             const int e = lane + 64 * i;
             const float l = e < E ? logits[wv * E + e] : 0.f;
             lg[wv][e] = l;
-            const uint32_t u = __float_as_uint(l + 0.0f);                   // -0 compares equal to +0
-            const uint32_t ord = u ^ ((u >> 31) ? 0xFFFFFFFFu : 0x80000000u);
-            kk[i] = e < E ? (((unsigned long long)ord << 32) | (uint32_t)(255 - e)) : 0ull;
+            kk[i] = e < E ? logit_key(l, e) : 0ull;
         }
         for (int j = 0; j < k; ++j) {
             const unsigned long long m1 = kk[0] > kk[1] ? kk[0] : kk[1];
             const unsigned long long m2 = kk[2] > kk[3] ? kk[2] : kk[3];
             const unsigned long long m = wave_max_u64(m1 > m2 ? m1 : m2);
-            if (lane == 0) sel[wv * k + j] = 255 - (int)(uint32_t)m;
+            if (lane == 0) sel[wv * k + j] = key_expert(m);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (kk[i] == m) kk[i] = 0ull;                               // keys are distinct: one owner
@@ -447,6 +417,19 @@ hipError_t launch_logits_small(const RouteArgs &a, hipStream_t st) {
 }
 
 bool small_logits_shape(int H) { return H == 4096 || H == 2048 || H == 1024 || H == 512 || H == 256; }
+
+hipError_t launch_route_logits(const RouteArgs &a, hipStream_t st) {
+    if (a.T <= SMALL_T && small_logits_shape(a.H)) {
+        if (a.x_bf16 && a.w_bf16) return launch_logits_small<true, true>(a, st);
+        if (a.x_bf16) return launch_logits_small<true, false>(a, st);
+        if (a.w_bf16) return launch_logits_small<false, true>(a, st);
+        return launch_logits_small<false, false>(a, st);
+    }
+    if (a.x_bf16 && a.w_bf16) return launch_logits<true, true>(a, st);
+    if (a.x_bf16) return launch_logits<true, false>(a, st);
+    if (a.w_bf16) return launch_logits<false, true>(a, st);
+    return launch_logits<false, false>(a, st);
+}
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
     hipError_t e;

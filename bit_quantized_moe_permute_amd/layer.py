@@ -11,7 +11,8 @@ import numpy as np
 import torch
 
 from . import (FMT_IQ2X, PATH_AUTO, LayerDesc, moe_combine, moe_combine_steer, moe_expert_ffn,
-               moe_expert_ffn_workspace, moe_prepare_weights, moe_route, moe_route_workspace, moe_weight_bytes)
+               moe_expert_ffn_workspace, moe_layer, moe_layer_workspace, moe_prepare_weights, moe_route,
+               moe_route_workspace, moe_weight_bytes)
 
 
 def _u8(a: np.ndarray, device) -> torch.Tensor:
@@ -119,25 +120,28 @@ class LayerBuffers:
     shared_out: torch.Tensor | None
     ws_ffn: torch.Tensor
     y: torch.Tensor
+    ws: torch.Tensor            # one buffer: ws_route and ws_ffn are views into it (the layout moe_layer takes)
 
     @classmethod
     def allocate(cls, L: DeviceLayer, T: int, with_logits: bool = False) -> "LayerBuffers":
         dev = L.device
         i32 = dict(dtype=torch.int32, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)
-        ws_r = moe_route_workspace(T, L.E, L.k)
-        ws_f = moe_expert_ffn_workspace(L.desc, T)
+        ws_r = (moe_route_workspace(T, L.E, L.k) + 255) // 256 * 256
+        ws_l = moe_layer_workspace(L.desc, T)
+        ws = torch.empty(max(ws_l, ws_r + 256), dtype=torch.uint8, device=dev)
         return cls(
             T=T,
             topk_idx=torch.empty(T, L.k, **i32), topk_w=torch.empty(T, L.k, **f32),
             logits=torch.empty(T, L.E, **f32) if with_logits else None,
             offsets=torch.empty(L.E + 1, **i32), perm=torch.empty(T * L.k, **i32),
             active=torch.empty(L.E + 1, **i32),
-            ws_route=torch.empty(max(ws_r, 256), dtype=torch.uint8, device=dev),
+            ws_route=ws[:ws_r],
             slot_out=torch.empty(T * L.k, L.H, **f32),
             shared_out=torch.empty(T, L.H, **f32) if L.Is else None,
-            ws_ffn=torch.empty(max(ws_f, 256), dtype=torch.uint8, device=dev),
+            ws_ffn=ws[ws_r:],
             y=torch.empty(T, L.H, **f32),
+            ws=ws,
         )
 
 
@@ -154,4 +158,13 @@ def forward(L: DeviceLayer, x: torch.Tensor, b: LayerBuffers, desc: LayerDesc | 
         moe_combine(b.slot_out, b.topk_w, b.shared_out, T, L.k, L.H, b.y, stream=stream)
     else:
         moe_combine_steer(b.slot_out, b.topk_w, b.shared_out, T, L.k, L.H, L.steer_v, L.steer_f, b.y, stream=stream)
+    return b.y
+
+
+def forward_layer(L: DeviceLayer, x: torch.Tensor, b: LayerBuffers, desc: LayerDesc | None = None, stream=None):
+    """The same layer as forward() through the single moe_layer call (one routing launch fewer at one token)."""
+    assert x.shape[0] == b.T
+    moe_layer(desc or L.desc, x, L.w_router, b.topk_idx, b.topk_w, b.offsets, b.perm, b.active, b.slot_out,
+              b.shared_out, b.y, b.ws, bias=L.bias, logits=b.logits, steer_v=L.steer_v, steer_f=L.steer_f,
+              stream=stream)
     return b.y

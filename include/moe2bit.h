@@ -271,6 +271,31 @@ moe_status moe_combine_steer(const float *slot_out, const float *topk_w, const f
                              int32_t top_k, int32_t hidden, const float *steer_v, float steer_f, float *y,
                              void *stream);
 
+/* Workspace bytes moe_layer needs for n_tokens tokens of layer L: the routing
+ * workspace rounded up to 256 bytes, then the expert-FFN workspace. */
+size_t moe_layer_workspace(const moe_layer_desc *L, int32_t n_tokens);
+
+/*
+ * The whole layer in one call: moe_route, moe_expert_ffn and moe_combine (or
+ * moe_combine_steer when steer_v is not NULL) with the same arguments, the
+ * same outputs, bit for bit, and the same checks -- w_router, w_dt and bias
+ * as in moe_route (its E and k are L's), steer_v and steer_f as in
+ * moe_combine_steer, y as in moe_combine.  ws (256-byte aligned, at least
+ * moe_layer_workspace(L, T) bytes) holds the routing workspace, then the
+ * expert-FFN workspace.  With one token on the decode kernels (bf16 x, k <= 16)
+ * the routing costs one launch instead of two: the logits kernel runs alone,
+ * and every routed gate/up workgroup selects the token's experts from the
+ * logits itself (the top-k rule and softmax of moe_route, in the same
+ * arithmetic), one of them writing topk_idx, topk_w, expert_offsets, perm and
+ * active for the down projection and the combine.  The one-token routing of
+ * moe_route is described in the route passage above: experts ordered by
+ * (descending logit, ascending index), softmax over the selected logits.
+ */
+moe_status moe_layer(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens, const void *w_router,
+                     int32_t w_dt, const float *bias, int32_t *topk_idx, float *topk_w, float *logits,
+                     int32_t *expert_offsets, int32_t *perm, int32_t *active, float *slot_out, float *shared_out,
+                     const float *steer_v, float steer_f, float *y, void *ws, size_t ws_bytes, void *stream);
+
 /*
  * Measurement helper, not part of the layer: reads `bytes` bytes of `buf`
  * (device, 16-byte aligned, a multiple of 16) once with 16-byte lane loads

@@ -639,3 +639,94 @@ def test_layer_zero_spike_and_mixed_scale_tokens(m, name, T, path):
     err = rel_l2_rows(got["y"], ref["y"])
     note(f"  max per-token rel L2 = {err.max():.3e}")
     assert err.max() <= TOL
+
+
+# ----------------------------------------------------------------------------
+# the single-call layer (moe_layer): same bits as the three calls
+# ----------------------------------------------------------------------------
+LAYER_CALL_CASES = [
+    # one token: routing selected inside the gate/up launch (MFMA iq2x kernel; VALU q4k kernel; top-16)
+    ("small", 1, False), ("decode", 1, False), ("decode", 1, True), ("small_q4k", 1, False),
+    ("small_mix_a", 1, False), ("small_mix_b", 1, False), ("mid_k16", 1, False), ("mid", 1, True),
+    # several tokens: the three calls inside one
+    ("small", 3, False), ("small", 37, True), ("mid", 70, False), ("tiny", 4, False),
+]
+
+
+@pytest.mark.parametrize("name,T,steer", LAYER_CALL_CASES, ids=[f"{a}-T{b}-s{int(c)}" for a, b, c in LAYER_CALL_CASES])
+def test_layer_call_matches_the_three_calls(m, name, T, steer):
+    """moe_layer writes the same routing outputs (indices, weights, offsets, permutation, active list, optional
+    logits), slot and shared outputs and layer output, bit for bit, as moe_route + moe_expert_ffn + moe_combine
+    (or moe_combine_steer); the one-token calls select their experts inside the gate/up launch."""
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward, forward_layer
+    L = _layer(name)
+    sp = L.spec
+    DL = DeviceLayer.from_synth(L)
+    if steer:
+        DL.set_steering(synth.steer_direction(sp.hidden), 1.0)
+    for r in range(3 if T == 1 else 1):
+        note(f"layer call {name} T={T} steer={steer} input {r}")
+        x = dev_x(synth.activations(name, T, sp.hidden, sp.x_bf16, seed=1700 + 10 * T + r))
+        for with_logits in (False, True):
+            b1 = LayerBuffers.allocate(DL, T, with_logits=with_logits)
+            b2 = LayerBuffers.allocate(DL, T, with_logits=with_logits)
+            b2.active.fill_(-5)
+            b2.offsets.fill_(-5)
+            forward(DL, x, b1)
+            forward_layer(DL, x, b2)
+            torch.cuda.synchronize()
+            n_act = int(b1.active[0])
+            assert torch.equal(b1.topk_idx, b2.topk_idx)
+            assert torch.equal(b1.topk_w, b2.topk_w)
+            assert torch.equal(b1.offsets, b2.offsets)
+            assert torch.equal(b1.perm, b2.perm)
+            assert torch.equal(b1.active[: n_act + 1], b2.active[: n_act + 1])
+            if with_logits:
+                assert torch.equal(b1.logits, b2.logits)
+            assert torch.equal(b1.slot_out, b2.slot_out)
+            if b1.shared_out is not None:
+                assert torch.equal(b1.shared_out, b2.shared_out)
+            assert torch.equal(b1.y, b2.y)
+    # and against the oracle once
+    xo = synth.activations(name, T, sp.hidden, sp.x_bf16, seed=1700 + 10 * T)
+    b = LayerBuffers.allocate(DL, T)
+    forward_layer(DL, dev_x(xo), b)
+    ref = oracle.layer(xo, L.w_router, sp.top_k, sp.n_experts, sp.inter, sp.gate_up_fmt, L.gate, L.up, sp.down_fmt,
+                       L.down, L.codebook, bias=L.bias, shared=L.shared,
+                       steering=(synth.steer_direction(sp.hidden), 1.0) if steer else None)
+    assert np.array_equal(b.topk_idx.cpu().numpy(), ref["topk_idx"])
+    err = rel_l2_rows(b.y.cpu().numpy(), ref["y"])
+    note(f"  max per-token rel L2 = {err.max():.3e}")
+    assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("name", ["mid", "decode"])
+def test_layer_call_graph_replay_matches_eager(m, name):
+    """moe_layer at one token captured once in a HIP graph: every replay on new inputs equals an eager call."""
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward_layer
+    note(f"layer call graph replay {name}")
+    L = _layer(name)
+    sp = L.spec
+    DL = DeviceLayer.from_synth(L)
+    xs = [dev_x(synth.activations(name, 1, sp.hidden, sp.x_bf16, seed=1800 + r)) for r in range(3)]
+    xin = torch.empty_like(xs[0])
+    xin.copy_(xs[0])
+    bg, be = LayerBuffers.allocate(DL, 1), LayerBuffers.allocate(DL, 1)
+    forward_layer(DL, xin, bg)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            forward_layer(DL, xin, bg)
+    torch.cuda.synchronize()
+    for r in range(3):
+        xin.copy_(xs[r])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        forward_layer(DL, xs[r], be)
+        torch.cuda.synchronize()
+        assert torch.equal(bg.topk_idx, be.topk_idx)
+        assert torch.equal(bg.y, be.y), f"replay {r}"
