@@ -119,7 +119,14 @@ size_t moe_weight_bytes(int32_t fmt, int64_t n_mats, int64_t rows, int64_t cols)
  * device, moe_weight_bytes(...) bytes, 16-byte aligned, must not overlap
  * `canonical`).  rows*cols must be a multiple of 256, and sub-blocks may not
  * straddle rows: cols % 32 == 0 (iq2x, q4k) or cols % 16 == 0 (q2k).
- * Offline step (weight load), not part of the per-token path.
+ * Offline step (weight load), not part of the per-token path.  The formats are
+ * the routed experts' storage on the pages (IQ2_XXS for up/gate, Q2_K for
+ * down, a 4-bit Q4_K variant: "antirez가 만든 DeepSeek V4 Flash 전용 로컬 추론 엔진
+ * ds4", summary bullets on 2-bit quantization and on the q4 model); the byte
+ * layouts above are this library's reading of those names.  The prepared
+ * layout holds the same bytes regrouped so one 16-byte lane load carries
+ * whole fields; it is private to the library.  Errors: MOE_ERR_INVALID_ARG
+ * for a bad shape, format, null, misaligned or overlapping buffer.
  */
 moe_status moe_prepare_weights(int32_t fmt, int64_t n_mats, int64_t rows, int64_t cols, const void *canonical,
                                void *prepared, void *stream);
@@ -129,7 +136,14 @@ moe_status moe_prepare_weights(int32_t fmt, int64_t n_mats, int64_t rows, int64_
  * n_mats stacked [rows][cols] matrices; matrices mat_begin .. mat_begin +
  * mat_count - 1 are written to out[mat_count*rows*cols] in row-major order,
  * every value exact.  codebook as in moe_layer_desc (iq2x only, else may be
- * NULL).
+ * NULL).  The dequantization formulas are the ones in the format table at the
+ * top of this file (the block structure the pages name: 256-weight blocks,
+ * fp16 block scale, per-32 group scale and per-8 codebook index with signs and
+ * parity for iq2x; 16 sub-blocks with 4-bit scale and min and fp16 d, dmin for
+ * q2k; 8 sub-blocks with 6-bit scale and min for q4k).  Every decoded weight
+ * is a product of at most 21 significant bits, so fp32 holds it exactly.
+ * Errors: MOE_ERR_INVALID_ARG for a bad shape, format, range, null or
+ * misaligned pointer.
  */
 moe_status moe_dequantize(int32_t fmt, const void *prepared, int64_t n_mats, int64_t rows, int64_t cols,
                           int64_t mat_begin, int64_t mat_count, const uint8_t *codebook, float *out, void *stream);
@@ -138,7 +152,14 @@ moe_status moe_dequantize(int32_t fmt, const void *prepared, int64_t n_mats, int
 size_t moe_route_workspace(int32_t n_tokens, int32_t n_experts, int32_t top_k);
 
 /*
- * Routing for T tokens.
+ * Routing for T tokens.  The router stays at full precision on the pages
+ * ("antirez가 만든 DeepSeek V4 Flash 전용 로컬 추론 엔진 ds4", summary bullets on
+ * 2-bit quantization: shared experts, projections and routing are not
+ * quantized); they do not say how its dot products are summed, and this
+ * library's reading is the fixed binary64 order below, so that the selected
+ * experts are reproducible bit for bit whatever the tiling.  Selection is a
+ * softmax top-k with ties to the lower expert index and weights renormalised
+ * over the selected experts.
  *   x [T][H] (x_dt), w_router [E][H] (w_dt), bias [E] fp32 or NULL.
  *   logit[t][e] = fp32( sum_h w[e][h] * x[t][h] ) (+ bias[e], added in fp64 to
  *     the fp32 logit and rounded to fp32), where the sum takes exact products
@@ -154,7 +175,10 @@ size_t moe_route_workspace(int32_t n_tokens, int32_t n_experts, int32_t top_k);
  *     expert_offsets is the exclusive scan of the per-expert counts;
  *     active[0] = number of experts with a slot, then those experts ascending.
  *   ws: workspace of at least moe_route_workspace(T, E, k) bytes.
- * Requires 1 <= T, H % 64 == 0, 1 <= k <= E <= 256.
+ * Requires 1 <= T, H % 64 == 0, 1 <= k <= E <= 256.  Errors:
+ * MOE_ERR_INVALID_ARG (null, misaligned, bad shape or dtype, workspace too
+ * small), MOE_ERR_DEVICE (launch failure).  All outputs are caller-owned
+ * device buffers; nothing is read back to the host.
  */
 moe_status moe_route(const void *x, int32_t x_dt, int32_t n_tokens, int32_t hidden, const void *w_router,
                      int32_t w_dt, int32_t n_experts, const float *bias, int32_t top_k, int32_t *topk_idx,
@@ -165,7 +189,14 @@ moe_status moe_route(const void *x, int32_t x_dt, int32_t n_tokens, int32_t hidd
 size_t moe_expert_ffn_workspace(const moe_layer_desc *L, int32_t n_tokens);
 
 /*
- * Routed and shared experts for T tokens.
+ * Routed and shared experts for T tokens: for every slot s = t*k + j the
+ * SwiGLU FFN of expert topk_idx[t][j] on x[t] with its 2-bit (or q4k) weights
+ * decoded exactly, and the bf16 shared expert on every token ("antirez가 만든
+ * DeepSeek V4 Flash 전용 로컬 추론 엔진 ds4", summary bullets on 2-bit
+ * quantization: the routed experts are the quantized part, the shared expert
+ * stays at full precision).  One token takes the decode kernels (each
+ * selected expert's blocks streamed once), up to 8 tokens the verify kernels,
+ * more the grouped-GEMM kernels over the token-to-expert permutation.
  *   x [T][H] (x_dt; fp32 activations take the generic kernels).
  *   topk_idx, expert_offsets, perm, active: as written by moe_route.
  *   slot_out [T*k][H] fp32: slot s = t*k + j gets FFN_{topk_idx[t][j]}(x[t]).
@@ -185,7 +216,9 @@ size_t moe_expert_ffn_workspace(const moe_layer_desc *L, int32_t n_tokens);
  * input scale for rows whose largest |x| lies between 2^-48 and 2^48 (beyond
  * that the clamp lets fp16 h or x over- or underflow); the tests cover x scaled
  * by 2^-20 .. 2^16 around unit RMS.  Non-finite inputs give non-finite
- * outputs.
+ * outputs.  Errors: MOE_ERR_INVALID_ARG (bad layer, null, misaligned,
+ * workspace too small), MOE_ERR_UNSUPPORTED (a forced kernel family that
+ * cannot take the shapes), MOE_ERR_DEVICE (launch failure).
  */
 moe_status moe_expert_ffn(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
                           const int32_t *topk_idx, const int32_t *expert_offsets, const int32_t *perm,
