@@ -101,10 +101,14 @@ moe_status moe_dequantize(int32_t fmt, const void *prepared, int64_t n_mats, int
                     "moe_dequantize");
 }
 
+// logits [T][E] fp32 | bounds of the matrix-core router: lo, hi [T][E] fp32, expert flags [E] int32
+static size_t route_logits_bytes(int32_t T, int32_t E) { return ((size_t)T * E * sizeof(float) + 255) / 256 * 256; }
+
 size_t moe_route_workspace(int32_t n_tokens, int32_t n_experts, int32_t top_k) {
     (void)top_k;
     if (n_tokens < 1 || n_experts < 1) return 0;
-    return ((size_t)n_tokens * n_experts * sizeof(float) + 255) / 256 * 256;
+    return route_logits_bytes(n_tokens, n_experts) +
+           ((2 * (size_t)n_tokens * n_experts + n_experts) * sizeof(float) + 255) / 256 * 256;
 }
 
 // Host checks of the routing arguments; fills `a` (logits scratch at ws).
@@ -131,6 +135,7 @@ static moe_status route_args(const char *fn, const void *x, int32_t x_dt, int32_
     a.topk_idx = topk_idx; a.topk_w = topk_w; a.logits_out = logits;
     a.offsets = expert_offsets; a.perm = perm; a.active = active;
     a.logits_ws = static_cast<float *>(ws);
+    a.bounds_ws = reinterpret_cast<float *>(static_cast<char *>(ws) + route_logits_bytes(n_tokens, n_experts));
     return MOE_OK;
 }
 

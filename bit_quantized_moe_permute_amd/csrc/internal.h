@@ -30,6 +30,7 @@ struct RouteArgs {
     float *logits_out;   // optional
     int32_t *offsets, *perm, *active;
     float *logits_ws;    // [T][E] scratch
+    float *bounds_ws;    // [2][T][E] fp32 + [E] int32 scratch of the bounded router (NULL: full binary64 router)
 };
 hipError_t launch_route(const RouteArgs &a, hipStream_t st);
 // the router logits alone (into a.logits_ws, and a.logits_out when set)

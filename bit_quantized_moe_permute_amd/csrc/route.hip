@@ -374,6 +374,274 @@ __global__ __launch_bounds__(1024) void k_select_small(const float *__restrict__
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Many tokens (prefill): bounded logits on the matrix cores, then the fixed-
+// order binary64 sum only where it can change the selection.
+//
+// k_router_bounds computes every logit in fp32 with bf16 MFMA (x and W_r are
+// bf16, so each product is exact) together with sum_h |w||x| (a second MFMA
+// on the magnitudes), and turns them into an interval [lo, hi] that provably
+// holds the fp32 logit the fixed-order binary64 sum gives (bias included):
+// whatever order and rounding the matrix cores use inside an accumulation,
+// each of its at most H + 8 roundings moves the result by at most 2^-23 of
+// sum |p|; the binary64 sum is within 80 * 2^-53 of it, and the final fp32
+// rounding within 2^-24 of its magnitude; products that underflow add at most
+// H * 2^-126.  k_router_select then takes, per token, the experts whose upper
+// bound reaches the k-th largest lower bound -- every other expert has k
+// experts certainly above it, even after the fp32 rounding that could make
+// logits tie -- recomputes exactly those logits with the fixed-order sum, and
+// selects and weights among them: indices and weights are those of the full
+// binary64 router, bit for bit.  Tokens or experts whose rows hold subnormal
+// bf16 values (which matrix cores may flush) and non-finite sums take the
+// exact sum for every expert.
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(16))) float rb_acc_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 rb_bf16x8_t;
+
+constexpr int RB_WAVES = 4;          // K quarters per workgroup
+
+__device__ __forceinline__ rb_acc_t rb_mfma(uint4 a, uint4 b, rb_acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(rb_bf16x8_t, a),
+                                                   __builtin_bit_cast(rb_bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ uint4 rb_abs(uint4 v) {
+    return make_uint4(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu);
+}
+// a nonzero bf16 with a zero exponent field in either half of the word
+__device__ __forceinline__ bool has_subnormal(uint32_t v) {
+    const uint32_t lo = v & 0x7FFFu, hi = (v >> 16) & 0x7FFFu;
+    return (lo != 0u && lo < 0x80u) || (hi != 0u && hi < 0x80u);
+}
+
+// Workgroups 0 .. n_tiles-1: a 32-token x 32-expert tile of bounds, wave w
+// summing the K quarter w, the quarters added in order; workgroups past that:
+// one expert row each, flagged in wflag when it holds a subnormal value.
+__global__ __launch_bounds__(256) void k_router_bounds(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+                                                       const float *__restrict__ bias, int T, int H, int E,
+                                                       float *__restrict__ lo, float *__restrict__ hi,
+                                                       int32_t *__restrict__ wflag, int n_tiles) {
+    __shared__ float red[2][RB_WAVES][16][64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if ((int)blockIdx.x >= n_tiles) {
+        const int e = blockIdx.x - n_tiles;
+        const uint4 *row = reinterpret_cast<const uint4 *>(w + (int64_t)e * H);
+        bool sub = false;
+        for (int i = tid; i < H / 8; i += blockDim.x) {
+            const uint4 v = row[i];
+            sub = sub || has_subnormal(v.x) || has_subnormal(v.y) || has_subnormal(v.z) || has_subnormal(v.w);
+        }
+        const int any = __syncthreads_or(sub ? 1 : 0);
+        if (tid == 0) wflag[e] = any;
+        return;
+    }
+    const int nte = (E + 31) / 32;
+    const int t0 = (blockIdx.x / nte) * 32, e0 = (blockIdx.x % nte) * 32;
+    const int r = lane & 31, hh = lane >> 5;
+    const uint16_t *xr = x + (int64_t)min(t0 + r, T - 1) * H + 32 * hh;
+    const uint16_t *wr = w + (int64_t)min(e0 + r, E - 1) * H + 32 * hh;
+    const int kq = H / RB_WAVES, kb = wv * kq;
+    rb_acc_t acc = {}, aac = {};
+    uint4 av[4], bv[4], na[4], nb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        av[j] = *reinterpret_cast<const uint4 *>(xr + kb + 8 * j);
+        bv[j] = *reinterpret_cast<const uint4 *>(wr + kb + 8 * j);
+    }
+    for (int k0 = kb; k0 < kb + kq; k0 += 64) {
+        const int kn = min(k0 + 64, kb + kq - 64);             // next chunk (the last one reloads itself)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            na[j] = *reinterpret_cast<const uint4 *>(xr + kn + 8 * j);
+            nb[j] = *reinterpret_cast<const uint4 *>(wr + kn + 8 * j);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc = rb_mfma(av[j], bv[j], acc);
+            aac = rb_mfma(rb_abs(av[j]), rb_abs(bv[j]), aac);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            av[j] = na[j];
+            bv[j] = nb[j];
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        red[0][wv][v][lane] = acc[v];
+        red[1][wv][v][lane] = aac[v];
+    }
+    __syncthreads();
+    // thread (wave q, lane l): outputs v = 4q .. 4q+3 of lane l's column
+    const double nr = (double)(H + 8);
+    const double eps = nr * 0x1p-23 * 1.0001;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int v = 4 * wv + i;
+        float a = red[0][0][v][lane], s = red[1][0][v][lane];
+#pragma unroll
+        for (int q = 1; q < RB_WAVES; ++q) {
+            a += red[0][q][v][lane];
+            s += red[1][q][v][lane];
+        }
+        const int t = t0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), e = e0 + (lane & 31);
+        if (t >= T || e >= E) continue;
+        float l32 = -INFINITY, h32 = INFINITY;
+        if (isfinite(a) && isfinite(s)) {
+            const double sat = (double)s / (1.0 - eps) + (double)H * 0x1p-126;    // >= sum |p| exactly
+            double b = eps * sat + (double)H * 0x1p-126 + nr * 0x1p-149 + 80.0 * 0x1p-53 * sat;
+            b += 0x1p-24 * (fabs((double)a) + b);
+            b *= 1.0 + 0x1p-40;
+            l32 = __double2float_rd((double)a - b);
+            h32 = __double2float_ru((double)a + b);
+            if (bias) {
+                l32 = (float)((double)l32 + (double)bias[e]);
+                h32 = (float)((double)h32 + (double)bias[e]);
+            }
+        }
+        lo[(int64_t)t * E + e] = l32;
+        hi[(int64_t)t * E + e] = h32;
+    }
+}
+
+// One wave per token: candidates from the bounds, their logits with the
+// fixed-order binary64 sum (the same operations as k_router_logits), top-k by
+// (descending logit, ascending index) among them, and the softmax over the
+// selected logits as k_topk computes it.  A candidate's router row is read
+// with 16-byte loads into the wave's LDS slice (the next candidate's row is
+// requested while the current one is summed), then lane p reads its strided
+// elements h = p + 64 j from there.
+// H = 64 * NJ (a multiple of 512 up to 4096)
+template <int NJ>
+__global__ __launch_bounds__(256) void k_router_select(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+                                                       const float *__restrict__ bias, int T, int E, int k,
+                                                       const float *__restrict__ lo, const float *__restrict__ hi,
+                                                       const int32_t *__restrict__ wflag,
+                                                       int32_t *__restrict__ topk_idx, float *__restrict__ topk_w) {
+    constexpr int H = 64 * NJ, NV = H / 512;                 // 16-byte loads per lane and router row
+    __shared__ uint4 wrow[4][2][H / 8];
+    __shared__ int clist[4][256];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wv;
+    if (t >= T) return;
+    uint32_t xb[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) xb[j] = x[(int64_t)t * H + lane + 64 * j];
+    uint32_t xp[NJ / 2];                                      // x[lane + 64 j] for j = 2i (low) and 2i + 1 (high)
+    bool xsub = false;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const uint32_t m7 = xb[j] & 0x7FFFu;
+        xsub = xsub || (m7 != 0u && m7 < 0x80u);
+    }
+#pragma unroll
+    for (int i = 0; i < NJ / 2; ++i) xp[i] = (xb[2 * i] & 0xFFFFu) | (xb[2 * i + 1] << 16);
+    const bool all = __ballot(xsub) != 0ull;
+    // the k-th largest lower bound (keys make equal bounds distinct)
+    float lv[4], hv[4];
+    unsigned long long kk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        lv[i] = e < E ? lo[(int64_t)t * E + e] : -INFINITY;
+        hv[i] = e < E ? hi[(int64_t)t * E + e] : -INFINITY;
+        kk[i] = e < E ? logit_key(lv[i], e) : 0ull;
+    }
+    unsigned long long m = 0ull;
+    for (int j = 0; j < k; ++j) {
+        const unsigned long long m1 = kk[0] > kk[1] ? kk[0] : kk[1];
+        const unsigned long long m2 = kk[2] > kk[3] ? kk[2] : kk[3];
+        m = wave_max_u64(m1 > m2 ? m1 : m2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (kk[i] == m) kk[i] = 0ull;
+    }
+    const float thr = lo[(int64_t)t * E + key_expert(m)];
+    // the candidates, listed in ascending expert order in the wave's LDS slice
+    bool cand[4];
+    int n_cand = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        cand[i] = e < E && (all || hv[i] >= thr || wflag[e] != 0 || !(hv[i] >= lv[i]));
+        const uint64_t bal = __ballot(cand[i]);
+        if (cand[i]) clist[wv][n_cand + __popcll(bal & ((1ull << lane) - 1ull))] = e;
+        n_cand += __popcll(bal);
+    }
+    __builtin_amdgcn_wave_barrier();
+    float lx[4] = {0.f, 0.f, 0.f, 0.f};
+    u32x4_t rv[NV];                                           // native vectors: kept in registers across the loop
+    {
+        const u32x4_t *row = reinterpret_cast<const u32x4_t *>(w + (int64_t)clist[wv][0] * H);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) rv[v] = row[v * 64 + lane];
+    }
+    for (int c = 0; c < n_cand; ++c) {
+        const int e = clist[wv][c];
+        u32x4_t *slot = reinterpret_cast<u32x4_t *>(wrow[wv][c & 1]);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) slot[v * 64 + lane] = rv[v];
+        {                                                     // the next row is in flight while this one is summed
+            const u32x4_t *row =
+                reinterpret_cast<const u32x4_t *>(w + (int64_t)clist[wv][min(c + 1, n_cand - 1)] * H);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) rv[v] = row[v * 64 + lane];
+        }
+        __builtin_amdgcn_wave_barrier();
+        const uint16_t *wr = reinterpret_cast<const uint16_t *>(slot);
+        double s = 0.0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const float xj = __uint_as_float((j & 1) ? (xp[j >> 1] & 0xFFFF0000u) : (xp[j >> 1] << 16));
+            s = __fma_rn((double)bf16_bits_to_f32(wr[lane + 64 * j]), (double)xj, s);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) s = s + __shfl_down(s, o, 64);
+        float l = (float)s;
+        if (bias) l = (float)((double)l + (double)bias[e]);
+        l = __shfl(l, 0, 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (lane + 64 * i == e) lx[i] = l;
+    }
+    // top-k among the candidates, then the weights (as k_topk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kk[i] = cand[i] ? logit_key(lx[i], lane + 64 * i) : 0ull;
+    float sel[4] = {0.f, 0.f, 0.f, 0.f}, l0 = 0.f;
+    for (int j = 0; j < k; ++j) {
+        const unsigned long long m1 = kk[0] > kk[1] ? kk[0] : kk[1];
+        const unsigned long long m2 = kk[2] > kk[3] ? kk[2] : kk[3];
+        const unsigned long long mm = wave_max_u64(m1 > m2 ? m1 : m2);
+        const int bi = key_expert(mm);
+        float bv = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (kk[i] == mm) kk[i] = 0ull;
+            if (lane + 64 * i == bi) bv = lx[i];
+        }
+        bv = __shfl(bv, bi & 63, 64);                      // the winner's logit, from the lane that holds it
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if ((j >> 6) == i && (j & 63) == lane) sel[i] = bv;
+        if (j == 0) l0 = bv;
+        if (lane == 0) topk_idx[(int64_t)t * k + j] = bi;
+    }
+    double ex[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ex[i] = exp((double)sel[i] - (double)l0);
+    double den = 0.0;
+    for (int jj = 0; jj < k; ++jj) {
+        const int i = jj >> 6;
+        const double vv = i == 0 ? ex[0] : (i == 1 ? ex[1] : (i == 2 ? ex[2] : ex[3]));
+        den += __shfl(vv, jj & 63, 64);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        if (j < k) topk_w[(int64_t)t * k + j] = (float)(ex[i] / den);
+    }
+}
+
 template <bool XB, bool WB>
 hipError_t launch_logits(const RouteArgs &a, hipStream_t st) {
     if (a.T == 1) {
@@ -431,8 +699,46 @@ hipError_t launch_route_logits(const RouteArgs &a, hipStream_t st) {
     return launch_logits<false, false>(a, st);
 }
 
+// The bounded matrix-core router applies to bf16 x and W_r, H a multiple of 512 up to 4096, many tokens, and no
+// request for the logits themselves (those come from the full binary64 router).
+bool bounded_route(const RouteArgs &a) {
+    return a.x_bf16 && a.w_bf16 && a.T > SMALL_T && a.H % 512 == 0 && a.H <= 4096 && !a.logits_out &&
+           a.bounds_ws != nullptr;
+}
+
 hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
     hipError_t e;
+    if (bounded_route(a)) {
+        float *lo = a.bounds_ws, *hi = a.bounds_ws + (size_t)a.T * a.E;
+        int32_t *wflag = reinterpret_cast<int32_t *>(hi + (size_t)a.T * a.E);
+        const int n_tiles = ((a.T + 31) / 32) * ((a.E + 31) / 32);
+        hipLaunchKernelGGL(k_router_bounds, dim3(n_tiles + a.E), dim3(256), 0, st,
+                           static_cast<const uint16_t *>(a.x), static_cast<const uint16_t *>(a.w), a.bias, a.T, a.H,
+                           a.E, lo, hi, wflag, n_tiles);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+#define MOE_SELECT(NJ_)                                                                                     \
+    case 64 * NJ_:                                                                                          \
+        hipLaunchKernelGGL(k_router_select<NJ_>, dim3((a.T + 3) / 4), dim3(256), 0, st,                    \
+                           static_cast<const uint16_t *>(a.x), static_cast<const uint16_t *>(a.w), a.bias, a.T,  \
+                           a.E, a.k, lo, hi, wflag, a.topk_idx, a.topk_w);                                   \
+        break;
+        switch (a.H) {
+            MOE_SELECT(64)
+            MOE_SELECT(56)
+            MOE_SELECT(48)
+            MOE_SELECT(40)
+            MOE_SELECT(32)
+            MOE_SELECT(24)
+            MOE_SELECT(16)
+            MOE_SELECT(8)
+            default: return hipErrorInvalidValue;
+        }
+#undef MOE_SELECT
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, st, a.topk_idx, a.T, a.k, a.E, a.offsets, a.perm,
+                           a.active);
+        return hipGetLastError();
+    }
     if (a.T <= SMALL_T && small_logits_shape(a.H)) {
         if (a.x_bf16 && a.w_bf16) e = launch_logits_small<true, true>(a, st);
         else if (a.x_bf16) e = launch_logits_small<true, false>(a, st);

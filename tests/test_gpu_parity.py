@@ -108,6 +108,23 @@ def _route_gpu(m, x, w_router, E, k, bias=None):
     return lg.cpu().numpy(), idx.cpu().numpy(), tw.cpu().numpy(), off.cpu().numpy(), perm.cpu().numpy(), act.cpu().numpy()
 
 
+def _route_gpu_no_logits(m, x, w_router, E, k, bias=None):
+    """moe_route without the logits output: above 8 tokens with bf16 inputs this takes the bounded matrix-core
+    router (exact binary64 sums only for the experts near each token's selection boundary)."""
+    T = x.shape[0]
+    i32 = dict(dtype=torch.int32, device="cuda")
+    idx = torch.empty(T, k, **i32)
+    tw = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    off = torch.empty(E + 1, **i32)
+    perm = torch.empty(T * k, **i32)
+    act = torch.full((E + 1,), -7, **i32)
+    ws = torch.empty(max(m.moe_route_workspace(T, E, k), 256), dtype=torch.uint8, device="cuda")
+    m.moe_route(dev_x(x), dev_x(w_router), E, k, idx, tw, off, perm, act, ws,
+                bias=None if bias is None else torch.from_numpy(bias).cuda())
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), tw.cpu().numpy(), off.cpu().numpy(), perm.cpu().numpy(), act.cpu().numpy()
+
+
 def _check_route(m, x, w_router, E, k, bias=None):
     lg, idx, tw, off, perm, act = _route_gpu(m, x, w_router, E, k, bias)
     ol, oi, ow = oracle.route(x, w_router, k, bias)
@@ -118,6 +135,13 @@ def _check_route(m, x, w_router, E, k, bias=None):
     assert np.array_equal(off, oo)
     assert np.array_equal(perm, op)
     assert np.array_equal(act[: oa[0] + 1], oa[: oa[0] + 1])
+    # without the logits output: the same bits (indices, weights, offsets, permutation, active list)
+    idx2, tw2, off2, perm2, act2 = _route_gpu_no_logits(m, x, w_router, E, k, bias)
+    assert np.array_equal(idx2, idx)
+    assert np.array_equal(tw2.view(np.uint32), tw.view(np.uint32))
+    assert np.array_equal(off2, off)
+    assert np.array_equal(perm2, perm)
+    assert np.array_equal(act2[: oa[0] + 1], oa[: oa[0] + 1])
 
 
 ROUTE_CASES = [
@@ -167,6 +191,57 @@ def test_route_full_size_decode_tokens(m):
     for i in range(8):
         _check_route(m, x[112 + 8 * i: 120 + 8 * i], wr, sp.n_experts, sp.top_k)
     note("route decode tokens: 64 x T=1, 16 x T=3, 8 x T=8")
+
+
+def _near_tie_router(H, E, seed):
+    """A bf16 router with duplicated rows (exact logit ties, broken by the lower index) and rows that differ from
+    another in one small entry (logits a few ulps apart)."""
+    wr, _ = synth.make_router("decode")
+    w = synth.bf16_bits_to_f32(wr[:E, :H]).copy()
+    g = np.random.default_rng(seed)
+    for a, b in ((5, 200), (17, 18), (0, 255), (100, 40)):
+        if max(a, b) < E:
+            w[b] = w[a]
+    for a, b in ((7, 8), (90, 91), (150, 30)):
+        if max(a, b) < E:
+            w[b] = w[a]
+            w[b, g.integers(H)] += np.float32(2.0 ** -12)
+    return synth.to_bf16_bits(w)
+
+
+@pytest.mark.parametrize("T", [9, 64, 300])
+def test_route_many_tokens_near_ties(m, T):
+    """Many-token routing on a router with duplicated and nearly duplicated expert rows, tokens built to sit near
+    the selection boundary (copies of a few tokens, a zero token), with and without a bias: the bounded
+    matrix-core router must give the full binary64 router's indices and weights bit for bit."""
+    note(f"route near ties T={T}")
+    H, E, k = 4096, 256, 8
+    w = _near_tie_router(H, E, T)
+    x = synth.activations("decode", T, H, True, seed=3100 + T).copy()
+    x[1] = 0
+    if T > 4:
+        x[3] = x[2]
+        x[4] = synth.to_bf16_bits(synth.bf16_bits_to_f32(x[2]) * np.float32(2.0 ** 9))
+    for bias in (None, synth.normal_f32(5, 9, (E,), 0.5)):
+        _check_route(m, x, w, E, k, bias)
+
+
+def test_route_many_tokens_subnormal_and_large_inputs(m):
+    """Tokens and router rows holding subnormal bf16 values (which matrix cores may flush: those tokens and experts
+    take the exact sum for every expert), tokens scaled by 2^40 and 2^-60, and a top-k of 1 and of 64."""
+    note("route subnormal / large inputs")
+    H, E, T = 2048, 96, 40
+    wr, _ = synth.make_router("small")
+    wf = synth.bf16_bits_to_f32(synth.make_router("decode")[0][:E, :H]).copy()
+    wf[3, 10] = np.float32(2.0 ** -130)                   # subnormal in bf16 (and fp32)
+    w = synth.to_bf16_bits(wf)
+    xf = synth.bf16_bits_to_f32(synth.activations("decode", T, H, True, seed=3200)).copy()
+    xf[5, 7] = np.float32(2.0 ** -128)
+    xf[6] *= np.float32(2.0 ** 40)
+    xf[7] *= np.float32(2.0 ** -60)
+    x = synth.to_bf16_bits(xf)
+    for k in (1, 8, 64):
+        _check_route(m, x, w, E, k)
 
 
 def test_route_summation_order_golden(m):
