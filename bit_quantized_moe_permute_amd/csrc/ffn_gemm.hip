@@ -289,62 +289,77 @@ __device__ __forceinline__ uint32_t lds_at(const uint32_t *tab, uint32_t byte_of
     return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(tab) + byte_off);
 }
 
-// One 256-wide K block: 16 K-steps x 2 B fragments x (1 or 2) token fragments.
-template <bool two>
-__device__ __forceinline__ void gu_block(const GuW &w, const uint4 *tile, const uint32_t *cb4, const uint32_t *sgn,
-                                         int n, int hh, float (&dprev)[2], f32x16_t (&acc)[2][2]) {
-    f16x2_t mul[2][4];                                   // [gate/up][group]: (2s+1), or 0 for a zero block
+// The codebook/sign word of K-step j (0..15) of matrix f in a block: a field is the 16-bit half of a word,
+// byte 0 the codebook row, byte 1 the sign index, each turned into a table byte offset by one sub-dword shift.
+__device__ __forceinline__ uint32_t gu_word(const GuW &w, int f, int j, const uint32_t *cb4, const uint32_t *sgn) {
+    const int chunk = j >> 3, fld = j & 7, p = fld & 3;
+    const uint4 qq = w.q[f][chunk];
+    const uint32_t dw = (fld >> 2) ? ((p < 2) ? qq.z : qq.w) : ((p < 2) ? qq.x : qq.y);
+    return (p & 1) ? (lds_at(cb4, byte_x4<2>(dw)) | lds_at(sgn, byte_x4<3>(dw)))
+                   : (lds_at(cb4, byte_x4<0>(dw)) | lds_at(sgn, byte_x4<1>(dw)));
+}
+
+// The decode state of one block: its 32 looked-up words, the group multipliers (2s+1) as packed fp16 (0 for a
+// zero block) and the block scales.
+struct GuS {
+    uint32_t words[2][16];
+    f16x2_t mul[2][4];
+    float d[2];
+};
+
+__device__ __forceinline__ void gu_scales(const GuW &w, GuS &st) {
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-        const float sf = rescale(w.d[f], dprev[f]);
-        scale_acc(acc[0][f], sf);
-        if constexpr (two) scale_acc(acc[1][f], sf);
+        st.d[f] = w.d[f];
         const uint32_t keep = w.d[f] == 0.f ? 0u : 0xFFFFFFFFu;
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
             const uint4 qq = w.q[f][gi >> 1];
             const uint32_t lo = (gi & 1) ? qq.z : qq.x, hi = (gi & 1) ? qq.w : qq.y;
-            mul[f][gi] = f16pair(iq2x_gscale(lo, hi) & keep);
+            st.mul[f][gi] = f16pair(iq2x_gscale(lo, hi) & keep);
         }
     }
-    // phase 1: all 32 codebook/sign lookups of the block at once (one LDS round trip); a field is the 16-bit
-    // half of a word: byte 0 the codebook row, byte 1 the sign index, each turned into a table byte offset by one
-    // sub-dword shift
-    uint32_t words[2][16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int chunk = j >> 3, fld = j & 7, p = fld & 3;
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            const uint4 qq = w.q[f][chunk];
-            const uint32_t dw = (fld >> 2) ? ((p < 2) ? qq.z : qq.w) : ((p < 2) ? qq.x : qq.y);
-            words[f][j] = (p & 1) ? (lds_at(cb4, byte_x4<2>(dw)) | lds_at(sgn, byte_x4<3>(dw)))
-                                  : (lds_at(cb4, byte_x4<0>(dw)) | lds_at(sgn, byte_x4<1>(dw)));
-        }
-    }
-    // phase 2: convert and multiply on the matrix cores; A fragments read one K-step ahead
+}
+
+// One 256-wide K block: 16 K-steps x 2 B fragments x (1 or 2) token fragments, from the decode state st, which it
+// refills with the next block's words (wn) in its second half: K-step 8 + i converts this block's words of steps
+// 8 + i and looks up the next block's words of steps i and 8 + i into the registers already converted, so the
+// next block's table lookups run under this block's products while its fields (requested at the start of this
+// block) have had half a block to arrive.  The gate accumulators are rescaled to the block's scale first, the up
+// accumulators only after the first gate products are issued (their last products of the previous block have
+// finished by then).
+template <bool two>
+__device__ __forceinline__ void gu_block(GuS &st, const GuW &wn, const uint4 *tile, const uint32_t *cb4,
+                                         const uint32_t *sgn, int n, int hh, float (&dprev)[2],
+                                         f32x16_t (&acc)[2][2]) {
+    const float s0 = rescale(st.d[0], dprev[0]), s1 = rescale(st.d[1], dprev[1]);
+    scale_acc(acc[0][0], s0);
+    if constexpr (two) scale_acc(acc[1][0], s0);
     auto col_chunk = [&](int j) {
         const int chunk = j >> 3, fld = j & 7;
         return 4 * (2 * hh + chunk + 4 * (fld >> 2)) + (fld & 3);   // 16-B chunk of column 32*grp + 8p
     };
-    f16x8_t a0 = frag16(tile, n, col_chunk(0)), a1;
-    if constexpr (two) a1 = frag16(tile, 32 + n, col_chunk(0));
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        f16x8_t na0, na1;
-        if (j + 1 < 16) {
-            na0 = frag16(tile, n, col_chunk(j + 1));
-            if constexpr (two) na1 = frag16(tile, 32 + n, col_chunk(j + 1));
+        const f16x8_t a0 = frag16(tile, n, col_chunk(j));
+        f16x8_t a1;
+        if constexpr (two) a1 = frag16(tile, 32 + n, col_chunk(j));
+        const f16x8_t b0 = fp4x8_f16_mul(st.words[0][j], st.mul[0][j >> 2]);
+        acc[0][0] = mfma_f16(a0, b0, acc[0][0]);
+        if constexpr (two) acc[1][0] = mfma_f16(a1, b0, acc[1][0]);
+        if (j == 0) {
+            scale_acc(acc[0][1], s1);
+            if constexpr (two) scale_acc(acc[1][1], s1);
         }
+        const f16x8_t b1 = fp4x8_f16_mul(st.words[1][j], st.mul[1][j >> 2]);
+        acc[0][1] = mfma_f16(a0, b1, acc[0][1]);
+        if constexpr (two) acc[1][1] = mfma_f16(a1, b1, acc[1][1]);
+        if (j >= 8) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            const f16x8_t b = fp4x8_f16_mul(words[f][j], mul[f][j >> 2]);
-            acc[0][f] = mfma_f16(a0, b, acc[0][f]);
-            if constexpr (two) acc[1][f] = mfma_f16(a1, b, acc[1][f]);
-        }
-        if (j + 1 < 16) {
-            a0 = na0;
-            if constexpr (two) a1 = na1;
+            for (int f = 0; f < 2; ++f) {
+                st.words[f][j - 8] = gu_word(wn, f, j - 8, cb4, sgn);
+                st.words[f][j] = gu_word(wn, f, j, cb4, sgn);
+            }
         }
     }
 }
@@ -355,27 +370,35 @@ __device__ __forceinline__ void gu_loop(const FfnArgs &a, int e, int row, int hh
                                         float (&dprev)[2], f32x16_t (&acc)[2][2]) {
     const int H = a.H, nkb = H / KB;
     const int64_t nb_row = H / KB, nb_mat = (int64_t)a.I * nb_row, NB = nb_mat * a.E;
-    GuW w0, w1;
+    GuW w;
+    GuS st;
     XStageN<two ? 4 : 2> xs;                             // a one-fragment tile needs its first 32 rows only
     x_fetch(src, 0, xs);
-    gu_load(a, e, row, 0, hh, nb_row, nb_mat, NB, w0);
+    gu_load(a, e, row, 0, hh, nb_row, nb_mat, NB, w);
     x_store(xs, tiles[0]);
-    __syncthreads();
-    // every iteration prefetches block min(kb + 1, nkb - 1): no conditional loads
+    __syncthreads();                                     // also publishes the tables
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        st.words[0][j] = gu_word(w, 0, j, cb4, sgn);
+        st.words[1][j] = gu_word(w, 1, j, cb4, sgn);
+    }
+    gu_scales(w, st);
     for (int kb = 0; kb < nkb; kb += 2) {
         const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
         x_fetch(src, k1 * KB, xs);
-        gu_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w1);
+        gu_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
-        gu_block<two>(w0, tiles[0], cb4, sgn, n, hh, dprev, acc);
+        gu_block<two>(st, w, tiles[0], cb4, sgn, n, hh, dprev, acc);
+        gu_scales(w, st);
         __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
         x_store(xs, tiles[1]);
         __syncthreads();
         if (kb + 1 >= nkb) break;
         x_fetch(src, k2 * KB, xs);
-        gu_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w0);
+        gu_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
-        gu_block<two>(w1, tiles[1], cb4, sgn, n, hh, dprev, acc);
+        gu_block<two>(st, w, tiles[1], cb4, sgn, n, hh, dprev, acc);
+        gu_scales(w, st);
         __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
         x_store(xs, tiles[0]);
         __syncthreads();
@@ -746,16 +769,36 @@ __device__ __forceinline__ void tile_sums(const uint4 *tile, _Float16 (*hs)[TOK]
     }
 }
 
+// The tile store of the down projection also writes each row's per-16 sums of h (q2k sub-blocks), as fp16 hi + lo,
+// from the registers that stage the tile: a 16-value sub-block is the two chunks of neighbouring threads.
+template <int NV>
+__device__ __forceinline__ void x_store_sums16(const XStageN<NV> &xs, uint4 *tile, _Float16 (*hs)[TOK][16]) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int idx = threadIdx.x + NTHR * i, m = idx >> 5, c = idx & 31;
+        tile[tpos(m, c)] = xs.v[i];
+        const uint32_t wds[4] = {xs.v[i].x, xs.v[i].y, xs.v[i].z, xs.v[i].w};
+        float sm = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const f16x2_t pr = __builtin_bit_cast(f16x2_t, wds[k]);
+            sm += (float)pr.x + (float)pr.y;
+        }
+        sm += __shfl_xor(sm, 1, 64);
+        if ((c & 1) == 0) {
+            const _Float16 hi = (_Float16)sm;
+            hs[0][m][c >> 1] = hi;
+            hs[1][m][c >> 1] = (_Float16)(sm - (float)hi);
+        }
+    }
+}
+
 template <bool two>
 __device__ __forceinline__ void dn_block(const DnW &w, const uint4 *tile, _Float16 (*hs)[TOK][16], int n, int hh,
                                          float &dprev, float &mprev, f32x16_t (&acc)[2], f32x16_t (&accm)[2]) {
     const float s1 = rescale(w.d, dprev), s2 = rescale(w.dm, mprev);
     scale_acc(acc[0], s1);
-    scale_acc(accm[0], s2);
-    if constexpr (two) {
-        scale_acc(acc[1], s1);
-        scale_acc(accm[1], s2);
-    }
+    if constexpr (two) scale_acc(acc[1], s1);
     const uint32_t kq = w.d == 0.f ? 0u : 0xFFu, km = w.dm == 0.f ? 0u : 0xFFu;
     f16x2_t scp[8];
     f16x8_t mins;
@@ -779,6 +822,8 @@ __device__ __forceinline__ void dn_block(const DnW &w, const uint4 *tile, _Float
         if constexpr (two) acc[1] = mfma_f16(frag16(tile, 32 + n, c), b, acc[1]);
     }
     // min term: K = the 16 sub-blocks; A = per-16 sums (hi, lo), B = mins
+    scale_acc(accm[0], s2);
+    if constexpr (two) scale_acc(accm[1], s2);
     accm[0] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[0][n][8 * hh]), mins, accm[0]);
     accm[0] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[1][n][8 * hh]), mins, accm[0]);
     if constexpr (two) {
@@ -789,7 +834,7 @@ __device__ __forceinline__ void dn_block(const DnW &w, const uint4 *tile, _Float
 
 template <bool two>
 __device__ __forceinline__ void dn_loop(const FfnArgs &a, int e, int row, int hh, int n, const uint16_t *const *src,
-                                        uint4 (*tiles)[TOK * 32], _Float16 (*hsum)[TOK][16], float &dprev,
+                                        uint4 (*tiles)[TOK * 32], _Float16 (*hsum)[2][TOK][16], float &dprev,
                                         float &mprev, f32x16_t (&acc)[2], f32x16_t (&accm)[2]) {
     const int I = a.I, H = a.H, nkb = I / KB;
     const int64_t nb_row = I / KB, nb_mat = (int64_t)H * nb_row, NB = nb_mat * a.E;
@@ -797,28 +842,24 @@ __device__ __forceinline__ void dn_loop(const FfnArgs &a, int e, int row, int hh
     XStageN<two ? 4 : 2> xs;                             // a one-fragment tile needs its first 32 rows only
     x_fetch(src, 0, xs);
     dn_load(a, e, row, 0, hh, nb_row, nb_mat, NB, w0);
-    x_store(xs, tiles[0]);
+    x_store_sums16(xs, tiles[0], hsum[0]);
     __syncthreads();
     for (int kb = 0; kb < nkb; kb += 2) {
         const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
-        tile_sums(tiles[0], hsum);
-        __syncthreads();
         x_fetch(src, k1 * KB, xs);
         dn_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w1);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
-        dn_block<two>(w0, tiles[0], hsum, n, hh, dprev, mprev, acc, accm);
+        dn_block<two>(w0, tiles[0], hsum[0], n, hh, dprev, mprev, acc, accm);
         __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
-        x_store(xs, tiles[1]);
+        x_store_sums16(xs, tiles[1], hsum[1]);
         __syncthreads();
         if (kb + 1 >= nkb) break;
-        tile_sums(tiles[1], hsum);
-        __syncthreads();
         x_fetch(src, k2 * KB, xs);
         dn_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w0);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
-        dn_block<two>(w1, tiles[1], hsum, n, hh, dprev, mprev, acc, accm);
+        dn_block<two>(w1, tiles[1], hsum[1], n, hh, dprev, mprev, acc, accm);
         __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
-        x_store(xs, tiles[0]);
+        x_store_sums16(xs, tiles[0], hsum[0]);
         __syncthreads();
     }
 }
@@ -889,7 +930,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
     __shared__ int dst[TOK];
     __shared__ float hfac[TOK];                                 // routed rows: 2^sigma of the row's token
     __shared__ uint4 tiles[2][TOK * 32];
-    __shared__ __attribute__((aligned(16))) _Float16 hsum[2][TOK][16];
+    __shared__ __attribute__((aligned(16))) _Float16 hsum[2][2][TOK][16];     // [tile buffer][hi, lo]
     Item it;
     if (!get_item(a, a.H, ROWS, a.H, tile_off, it)) return;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -918,8 +959,8 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
         if constexpr (FD == FMT_Q4K) {
             const int nkb = I / KB;
             const int64_t NB = (int64_t)a.E * H * nkb, bl0 = ((int64_t)it.e * H + row) * nkb;
-            if (two) q4_loop<true>(a.down, NB, bl0, nkb, n, hh, src, tiles, hsum, dprev, mprev, acc, accm);
-            else q4_loop<false>(a.down, NB, bl0, nkb, n, hh, src, tiles, hsum, dprev, mprev, acc, accm);
+            if (two) q4_loop<true>(a.down, NB, bl0, nkb, n, hh, src, tiles, hsum[0], dprev, mprev, acc, accm);
+            else q4_loop<false>(a.down, NB, bl0, nkb, n, hh, src, tiles, hsum[0], dprev, mprev, acc, accm);
         } else {
             if (two) dn_loop<true>(a, it.e, row, hh, n, src, tiles, hsum, dprev, mprev, acc, accm);
             else dn_loop<false>(a, it.e, row, hh, n, src, tiles, hsum, dprev, mprev, acc, accm);
