@@ -656,6 +656,33 @@ def prefill_bench(L, DL, reps, names, samples=None):
         }
         log(f"prefill {name}: {T_total / wall:.0f} tokens/s, gate/up stage {gu_us:.1f} us ({gu_tf:.0f} TFLOP/s), "
             f"down stage {dn_us:.1f} us ({dn_tf:.0f} TFLOP/s)")
+        if sp.down_fmt == 2:
+            # the approximate fast mode (opt-in): q2k down weights as one fp16 fused multiply-add each, the shared
+            # expert's h in one bf16 plane; checked against the oracle at 5e-3 by the test suite
+            from bit_quantized_moe_permute_amd import PRECISION_FAST
+            fdesc = DL.make_desc(precision=PRECISION_FAST)
+
+            def prompt_fast():
+                for c0_, n_ in chunks:
+                    forward_layer(DL, xd[c0_:c0_ + n_], bufs[n_], desc=fdesc)
+
+            prompt_fast()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                prompt_fast()
+            torch.cuda.synchronize()
+            fwall = (time.perf_counter() - t0) / reps
+            forward_layer(DL, xc, b, desc=fdesc)
+            fdn_us = graph_time_us(lambda i: moe_expert_down(fdesc, xc, b.topk_idx, b.offsets, b.perm, b.active,
+                                                             b.slot_out, b.shared_out, b.ws_ffn), reps)
+            out[name]["fast_mode"] = {"tokens_per_s": round(T_total / fwall, 1), "ms_per_prompt": round(fwall * 1e3, 4),
+                                      "speedup": round(wall / fwall, 3), "down_stage_us": round(fdn_us, 2),
+                                      "tolerance": 5e-3}
+            log(f"prefill {name} fast mode: {T_total / fwall:.0f} tokens/s ({wall / fwall:.2f}x), down stage "
+                f"{fdn_us:.1f} us")
+            forward_layer(DL, xc, b)
+            torch.cuda.synchronize()
         if samples is not None:
             rows_all = []
             for ci, (c0, n) in enumerate(chunks):

@@ -19,7 +19,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE = 0, 1, 2, 3
 DT_F32, DT_BF16 = 0, 1
 FMT_IQ2X, FMT_Q2K, FMT_Q4K = 1, 2, 3
 PATH_AUTO, PATH_GENERIC, PATH_GEMV, PATH_GEMM = 0, 1, 2, 3
-ABI_VERSION = 2
+PRECISION_EXACT, PRECISION_FAST = 0, 1
+ABI_VERSION = 3
 
 EXPORTS = [
     "moe_abi_version", "moe_last_error", "moe_weight_bytes", "moe_prepare_weights", "moe_dequantize",
@@ -45,6 +46,7 @@ class LayerDesc(ctypes.Structure):
         ("shared_inter", ctypes.c_int32),
         ("shared_gate", ctypes.c_void_p), ("shared_up", ctypes.c_void_p), ("shared_down", ctypes.c_void_p),
         ("path", ctypes.c_int32),
+        ("precision", ctypes.c_int32),
     ]
 
 

@@ -178,6 +178,8 @@ static moe_status check_layer(const moe_layer_desc *L, const char *fn) {
             return fail(MOE_ERR_INVALID_ARG, "%s: shared expert dims must be multiples of 8", fn);
     }
     if (L->path < MOE_PATH_AUTO || L->path > MOE_PATH_GEMM) return fail(MOE_ERR_INVALID_ARG, "%s: unknown path", fn);
+    if (L->precision != MOE_PRECISION_EXACT && L->precision != MOE_PRECISION_FAST)
+        return fail(MOE_ERR_INVALID_ARG, "%s: unknown precision", fn);
     return MOE_OK;
 }
 
@@ -195,6 +197,7 @@ static moe::FfnArgs make_args(const moe_layer_desc *L, const void *x, int x_dt, 
     a.su = static_cast<const uint16_t *>(L->shared_up);
     a.sd = static_cast<const uint16_t *>(L->shared_down);
     a.x = x; a.x_bf16 = x_dt == MOE_DT_BF16;
+    a.fast = L->precision == MOE_PRECISION_FAST;
     return a;
 }
 

@@ -289,77 +289,62 @@ __device__ __forceinline__ uint32_t lds_at(const uint32_t *tab, uint32_t byte_of
     return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(tab) + byte_off);
 }
 
-// The codebook/sign word of K-step j (0..15) of matrix f in a block: a field is the 16-bit half of a word,
-// byte 0 the codebook row, byte 1 the sign index, each turned into a table byte offset by one sub-dword shift.
-__device__ __forceinline__ uint32_t gu_word(const GuW &w, int f, int j, const uint32_t *cb4, const uint32_t *sgn) {
-    const int chunk = j >> 3, fld = j & 7, p = fld & 3;
-    const uint4 qq = w.q[f][chunk];
-    const uint32_t dw = (fld >> 2) ? ((p < 2) ? qq.z : qq.w) : ((p < 2) ? qq.x : qq.y);
-    return (p & 1) ? (lds_at(cb4, byte_x4<2>(dw)) | lds_at(sgn, byte_x4<3>(dw)))
-                   : (lds_at(cb4, byte_x4<0>(dw)) | lds_at(sgn, byte_x4<1>(dw)));
-}
-
-// The decode state of one block: its 32 looked-up words, the group multipliers (2s+1) as packed fp16 (0 for a
-// zero block) and the block scales.
-struct GuS {
-    uint32_t words[2][16];
-    f16x2_t mul[2][4];
-    float d[2];
-};
-
-__device__ __forceinline__ void gu_scales(const GuW &w, GuS &st) {
+// One 256-wide K block: 16 K-steps x 2 B fragments x (1 or 2) token fragments.
+template <bool two>
+__device__ __forceinline__ void gu_block(const GuW &w, const uint4 *tile, const uint32_t *cb4, const uint32_t *sgn,
+                                         int n, int hh, float (&dprev)[2], f32x16_t (&acc)[2][2]) {
+    f16x2_t mul[2][4];                                   // [gate/up][group]: (2s+1), or 0 for a zero block
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-        st.d[f] = w.d[f];
+        const float sf = rescale(w.d[f], dprev[f]);
+        scale_acc(acc[0][f], sf);
+        if constexpr (two) scale_acc(acc[1][f], sf);
         const uint32_t keep = w.d[f] == 0.f ? 0u : 0xFFFFFFFFu;
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
             const uint4 qq = w.q[f][gi >> 1];
             const uint32_t lo = (gi & 1) ? qq.z : qq.x, hi = (gi & 1) ? qq.w : qq.y;
-            st.mul[f][gi] = f16pair(iq2x_gscale(lo, hi) & keep);
+            mul[f][gi] = f16pair(iq2x_gscale(lo, hi) & keep);
         }
     }
-}
-
-// One 256-wide K block: 16 K-steps x 2 B fragments x (1 or 2) token fragments, from the decode state st, which it
-// refills with the next block's words (wn) in its second half: K-step 8 + i converts this block's words of steps
-// 8 + i and looks up the next block's words of steps i and 8 + i into the registers already converted, so the
-// next block's table lookups run under this block's products while its fields (requested at the start of this
-// block) have had half a block to arrive.  The gate accumulators are rescaled to the block's scale first, the up
-// accumulators only after the first gate products are issued (their last products of the previous block have
-// finished by then).
-template <bool two>
-__device__ __forceinline__ void gu_block(GuS &st, const GuW &wn, const uint4 *tile, const uint32_t *cb4,
-                                         const uint32_t *sgn, int n, int hh, float (&dprev)[2],
-                                         f32x16_t (&acc)[2][2]) {
-    const float s0 = rescale(st.d[0], dprev[0]), s1 = rescale(st.d[1], dprev[1]);
-    scale_acc(acc[0][0], s0);
-    if constexpr (two) scale_acc(acc[1][0], s0);
+    // phase 1: all 32 codebook/sign lookups of the block at once (one LDS round trip); a field is the 16-bit
+    // half of a word: byte 0 the codebook row, byte 1 the sign index, each turned into a table byte offset by one
+    // sub-dword shift
+    uint32_t words[2][16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int chunk = j >> 3, fld = j & 7, p = fld & 3;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const uint4 qq = w.q[f][chunk];
+            const uint32_t dw = (fld >> 2) ? ((p < 2) ? qq.z : qq.w) : ((p < 2) ? qq.x : qq.y);
+            words[f][j] = (p & 1) ? (lds_at(cb4, byte_x4<2>(dw)) | lds_at(sgn, byte_x4<3>(dw)))
+                                  : (lds_at(cb4, byte_x4<0>(dw)) | lds_at(sgn, byte_x4<1>(dw)));
+        }
+    }
+    // phase 2: convert and multiply on the matrix cores; A fragments read one K-step ahead
     auto col_chunk = [&](int j) {
         const int chunk = j >> 3, fld = j & 7;
         return 4 * (2 * hh + chunk + 4 * (fld >> 2)) + (fld & 3);   // 16-B chunk of column 32*grp + 8p
     };
+    f16x8_t a0 = frag16(tile, n, col_chunk(0)), a1;
+    if constexpr (two) a1 = frag16(tile, 32 + n, col_chunk(0));
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        const f16x8_t a0 = frag16(tile, n, col_chunk(j));
-        f16x8_t a1;
-        if constexpr (two) a1 = frag16(tile, 32 + n, col_chunk(j));
-        const f16x8_t b0 = fp4x8_f16_mul(st.words[0][j], st.mul[0][j >> 2]);
-        acc[0][0] = mfma_f16(a0, b0, acc[0][0]);
-        if constexpr (two) acc[1][0] = mfma_f16(a1, b0, acc[1][0]);
-        if (j == 0) {
-            scale_acc(acc[0][1], s1);
-            if constexpr (two) scale_acc(acc[1][1], s1);
+        f16x8_t na0, na1;
+        if (j + 1 < 16) {
+            na0 = frag16(tile, n, col_chunk(j + 1));
+            if constexpr (two) na1 = frag16(tile, 32 + n, col_chunk(j + 1));
         }
-        const f16x8_t b1 = fp4x8_f16_mul(st.words[1][j], st.mul[1][j >> 2]);
-        acc[0][1] = mfma_f16(a0, b1, acc[0][1]);
-        if constexpr (two) acc[1][1] = mfma_f16(a1, b1, acc[1][1]);
-        if (j >= 8) {
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                st.words[f][j - 8] = gu_word(wn, f, j - 8, cb4, sgn);
-                st.words[f][j] = gu_word(wn, f, j, cb4, sgn);
-            }
+        for (int f = 0; f < 2; ++f) {
+            const f16x8_t b = fp4x8_f16_mul(words[f][j], mul[f][j >> 2]);
+            acc[0][f] = mfma_f16(a0, b, acc[0][f]);
+            if constexpr (two) acc[1][f] = mfma_f16(a1, b, acc[1][f]);
+        }
+        if (j + 1 < 16) {
+            a0 = na0;
+            if constexpr (two) a1 = na1;
         }
     }
 }
@@ -370,35 +355,27 @@ __device__ __forceinline__ void gu_loop(const FfnArgs &a, int e, int row, int hh
                                         float (&dprev)[2], f32x16_t (&acc)[2][2]) {
     const int H = a.H, nkb = H / KB;
     const int64_t nb_row = H / KB, nb_mat = (int64_t)a.I * nb_row, NB = nb_mat * a.E;
-    GuW w;
-    GuS st;
+    GuW w0, w1;
     XStageN<two ? 4 : 2> xs;                             // a one-fragment tile needs its first 32 rows only
     x_fetch(src, 0, xs);
-    gu_load(a, e, row, 0, hh, nb_row, nb_mat, NB, w);
+    gu_load(a, e, row, 0, hh, nb_row, nb_mat, NB, w0);
     x_store(xs, tiles[0]);
-    __syncthreads();                                     // also publishes the tables
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        st.words[0][j] = gu_word(w, 0, j, cb4, sgn);
-        st.words[1][j] = gu_word(w, 1, j, cb4, sgn);
-    }
-    gu_scales(w, st);
+    __syncthreads();
+    // every iteration prefetches block min(kb + 1, nkb - 1): no conditional loads
     for (int kb = 0; kb < nkb; kb += 2) {
         const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
         x_fetch(src, k1 * KB, xs);
-        gu_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w);
+        gu_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w1);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
-        gu_block<two>(st, w, tiles[0], cb4, sgn, n, hh, dprev, acc);
-        gu_scales(w, st);
+        gu_block<two>(w0, tiles[0], cb4, sgn, n, hh, dprev, acc);
         __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
         x_store(xs, tiles[1]);
         __syncthreads();
         if (kb + 1 >= nkb) break;
         x_fetch(src, k2 * KB, xs);
-        gu_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w);
+        gu_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w0);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
-        gu_block<two>(st, w, tiles[1], cb4, sgn, n, hh, dprev, acc);
-        gu_scales(w, st);
+        gu_block<two>(w1, tiles[1], cb4, sgn, n, hh, dprev, acc);
         __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
         x_store(xs, tiles[0]);
         __syncthreads();
@@ -606,7 +583,7 @@ __device__ __forceinline__ void sg_loop(const FfnArgs &a, int row, int hh, int n
 // rows per item, SwiGLU in registers).  q4k: waves 0-3 own 32 gate rows each,
 // waves 4-7 the same 128 rows of up (128 rows per item); the up values meet
 // the gate values in LDS for the SwiGLU.
-template <int FG>
+template <int FG, bool FAST>
 __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
     const FfnArgs &a = g.a;
     constexpr int RPI = FG == FMT_Q4K ? ROWS / 2 : ROWS;
@@ -718,7 +695,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_gateup(GemmArgs g) {
                     const uint32_t lo = (rb + 0x7FFFu + ((rb >> 16) & 1u)) >> 16;
                     const int64_t o = (int64_t)d * a.Is + row;
                     g.hs_hi[o] = (uint16_t)hi;
-                    g.hs_lo[o] = (uint16_t)lo;
+                    if constexpr (!FAST) g.hs_lo[o] = (uint16_t)lo;
                 }
             }
     }
@@ -769,36 +746,16 @@ __device__ __forceinline__ void tile_sums(const uint4 *tile, _Float16 (*hs)[TOK]
     }
 }
 
-// The tile store of the down projection also writes each row's per-16 sums of h (q2k sub-blocks), as fp16 hi + lo,
-// from the registers that stage the tile: a 16-value sub-block is the two chunks of neighbouring threads.
-template <int NV>
-__device__ __forceinline__ void x_store_sums16(const XStageN<NV> &xs, uint4 *tile, _Float16 (*hs)[TOK][16]) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int idx = threadIdx.x + NTHR * i, m = idx >> 5, c = idx & 31;
-        tile[tpos(m, c)] = xs.v[i];
-        const uint32_t wds[4] = {xs.v[i].x, xs.v[i].y, xs.v[i].z, xs.v[i].w};
-        float sm = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const f16x2_t pr = __builtin_bit_cast(f16x2_t, wds[k]);
-            sm += (float)pr.x + (float)pr.y;
-        }
-        sm += __shfl_xor(sm, 1, 64);
-        if ((c & 1) == 0) {
-            const _Float16 hi = (_Float16)sm;
-            hs[0][m][c >> 1] = hi;
-            hs[1][m][c >> 1] = (_Float16)(sm - (float)hi);
-        }
-    }
-}
-
 template <bool two>
 __device__ __forceinline__ void dn_block(const DnW &w, const uint4 *tile, _Float16 (*hs)[TOK][16], int n, int hh,
                                          float &dprev, float &mprev, f32x16_t (&acc)[2], f32x16_t (&accm)[2]) {
     const float s1 = rescale(w.d, dprev), s2 = rescale(w.dm, mprev);
     scale_acc(acc[0], s1);
-    if constexpr (two) scale_acc(acc[1], s1);
+    scale_acc(accm[0], s2);
+    if constexpr (two) {
+        scale_acc(acc[1], s1);
+        scale_acc(accm[1], s2);
+    }
     const uint32_t kq = w.d == 0.f ? 0u : 0xFFu, km = w.dm == 0.f ? 0u : 0xFFu;
     f16x2_t scp[8];
     f16x8_t mins;
@@ -822,8 +779,6 @@ __device__ __forceinline__ void dn_block(const DnW &w, const uint4 *tile, _Float
         if constexpr (two) acc[1] = mfma_f16(frag16(tile, 32 + n, c), b, acc[1]);
     }
     // min term: K = the 16 sub-blocks; A = per-16 sums (hi, lo), B = mins
-    scale_acc(accm[0], s2);
-    if constexpr (two) scale_acc(accm[1], s2);
     accm[0] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[0][n][8 * hh]), mins, accm[0]);
     accm[0] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[1][n][8 * hh]), mins, accm[0]);
     if constexpr (two) {
@@ -834,7 +789,7 @@ __device__ __forceinline__ void dn_block(const DnW &w, const uint4 *tile, _Float
 
 template <bool two>
 __device__ __forceinline__ void dn_loop(const FfnArgs &a, int e, int row, int hh, int n, const uint16_t *const *src,
-                                        uint4 (*tiles)[TOK * 32], _Float16 (*hsum)[2][TOK][16], float &dprev,
+                                        uint4 (*tiles)[TOK * 32], _Float16 (*hsum)[TOK][16], float &dprev,
                                         float &mprev, f32x16_t (&acc)[2], f32x16_t (&accm)[2]) {
     const int I = a.I, H = a.H, nkb = I / KB;
     const int64_t nb_row = I / KB, nb_mat = (int64_t)H * nb_row, NB = nb_mat * a.E;
@@ -842,24 +797,137 @@ __device__ __forceinline__ void dn_loop(const FfnArgs &a, int e, int row, int hh
     XStageN<two ? 4 : 2> xs;                             // a one-fragment tile needs its first 32 rows only
     x_fetch(src, 0, xs);
     dn_load(a, e, row, 0, hh, nb_row, nb_mat, NB, w0);
-    x_store_sums16(xs, tiles[0], hsum[0]);
+    x_store(xs, tiles[0]);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; kb += 2) {
+        const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
+        tile_sums(tiles[0], hsum);
+        __syncthreads();
+        x_fetch(src, k1 * KB, xs);
+        dn_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w1);
+        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
+        dn_block<two>(w0, tiles[0], hsum, n, hh, dprev, mprev, acc, accm);
+        __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
+        x_store(xs, tiles[1]);
+        __syncthreads();
+        if (kb + 1 >= nkb) break;
+        tile_sums(tiles[1], hsum);
+        __syncthreads();
+        x_fetch(src, k2 * KB, xs);
+        dn_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w0);
+        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
+        dn_block<two>(w1, tiles[1], hsum, n, hh, dprev, mprev, acc, accm);
+        __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
+        x_store(xs, tiles[0]);
+        __syncthreads();
+    }
+}
+
+// Fast mode (approximate, opt-in): every weight becomes one fp16 value, q * fp16(d sc) - fp16(dmin m) in a fused
+// packed multiply-add, so neither the per-16 sums of h, nor the min products, nor rescaling between blocks remain.
+template <bool two>
+__device__ __forceinline__ void dn_block_fast(const DnW &w, const uint4 *tile, int n, int hh, f32x16_t (&acc)[2]) {
+    f16x2_t dsc[8], nmn[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t byte = (i < 4 ? w.sm.x >> (8 * i) : w.sm.y >> (8 * (i - 4))) & 0xFFu;
+        const _Float16 a = (_Float16)(w.d * (float)(byte & 15u)), b = (_Float16)(-w.dm * (float)(byte >> 4));
+        dsc[i] = f16x2_t{a, a};
+        nmn[i] = f16x2_t{b, b};
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int sbl = j >> 1, half = j & 1;
+        const int c = 2 * (8 * hh + sbl) + half;
+        const f16x8_t a0 = frag16(tile, n, c);
+        const uint4 qq = w.q[sbl >> 2];
+        const uint32_t dw = (sbl & 3) == 0 ? qq.x : ((sbl & 3) == 1 ? qq.y : ((sbl & 3) == 2 ? qq.z : qq.w));
+        const uint32_t codes = half ? ((dw >> 2) & 0x33333333u) : (dw & 0x33333333u);
+        const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 2.0f, 0);   // q, exact
+        const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 2.0f, 1);
+        const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 2.0f, 2);
+        const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 2.0f, 3);
+        const f16x2_t w0 = __builtin_elementwise_fma(p0, dsc[sbl], nmn[sbl]);
+        const f16x2_t w1 = __builtin_elementwise_fma(p1, dsc[sbl], nmn[sbl]);
+        const f16x2_t w2 = __builtin_elementwise_fma(p2, dsc[sbl], nmn[sbl]);
+        const f16x2_t w3 = __builtin_elementwise_fma(p3, dsc[sbl], nmn[sbl]);
+        const f16x8_t b = f16x8_t{w0.x, w0.y, w1.x, w1.y, w2.x, w2.y, w3.x, w3.y};
+        acc[0] = mfma_f16(a0, b, acc[0]);
+        if constexpr (two) acc[1] = mfma_f16(frag16(tile, 32 + n, c), b, acc[1]);
+    }
+}
+
+template <bool two>
+__device__ __forceinline__ void dn_loop_fast(const FfnArgs &a, int e, int row, int hh, int n,
+                                             const uint16_t *const *src, uint4 (*tiles)[TOK * 32],
+                                             f32x16_t (&acc)[2]) {
+    const int I = a.I, H = a.H, nkb = I / KB;
+    const int64_t nb_row = I / KB, nb_mat = (int64_t)H * nb_row, NB = nb_mat * a.E;
+    DnW w0, w1;
+    XStageN<two ? 4 : 2> xs;
+    x_fetch(src, 0, xs);
+    dn_load(a, e, row, 0, hh, nb_row, nb_mat, NB, w0);
+    x_store(xs, tiles[0]);
     __syncthreads();
     for (int kb = 0; kb < nkb; kb += 2) {
         const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
         x_fetch(src, k1 * KB, xs);
         dn_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w1);
-        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
-        dn_block<two>(w0, tiles[0], hsum[0], n, hh, dprev, mprev, acc, accm);
-        __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
-        x_store_sums16(xs, tiles[1], hsum[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        dn_block_fast<two>(w0, tiles[0], n, hh, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        x_store(xs, tiles[1]);
         __syncthreads();
         if (kb + 1 >= nkb) break;
         x_fetch(src, k2 * KB, xs);
         dn_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w0);
-        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
-        dn_block<two>(w1, tiles[1], hsum[1], n, hh, dprev, mprev, acc, accm);
-        __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
-        x_store_sums16(xs, tiles[0], hsum[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        dn_block_fast<two>(w1, tiles[1], n, hh, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        x_store(xs, tiles[0]);
+        __syncthreads();
+    }
+}
+
+// Shared expert down in fast mode: A = h as one bf16 plane (256-wide K blocks), B = the bf16 rows, 8 K-steps of
+// B read one half-block ahead.
+template <bool two>
+__device__ __forceinline__ void sd_half_fast(const bf16x8_t (&b)[8], const uint4 *tile, int half, int n, int hh,
+                                             f32x16_t (&acc)[2]) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+        const int c = 16 * half + 2 * jj + hh;            // columns 128 half + 16 jj + 8 hh
+        acc[0] = mfma_bf16(fragbf(tile, n, c), b[jj], acc[0]);
+        if constexpr (two) acc[1] = mfma_bf16(fragbf(tile, 32 + n, c), b[jj], acc[1]);
+    }
+}
+
+template <bool two>
+__device__ __forceinline__ void sd_loop_fast(const FfnArgs &a, int row, int hh, int n, const uint16_t *const *hi,
+                                             uint4 (*tiles)[TOK * 32], f32x16_t (&acc)[2]) {
+    const int nkb = a.Is / KB;
+    bf16x8_t b0[8], b1[8];
+    XStage xs;
+    auto bload = [&](int st, bf16x8_t (&b)[8]) {         // K-steps of the 128-wide stage st
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            b[jj] = *reinterpret_cast<const bf16x8_t *>(a.sd + (int64_t)row * a.Is + st * 128 + 16 * jj + 8 * hh);
+    };
+    x_fetch(hi, 0, xs);
+    bload(0, b0);
+    x_store(xs, tiles[0]);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int k1 = min(kb + 1, nkb - 1);
+        x_fetch(hi, k1 * KB, xs);
+        bload(2 * kb + 1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        sd_half_fast<two>(b0, tiles[kb & 1], 0, n, hh, acc);
+        bload(2 * k1, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        sd_half_fast<two>(b1, tiles[kb & 1], 1, n, hh, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        x_store(xs, tiles[(kb + 1) & 1]);
         __syncthreads();
     }
 }
@@ -921,7 +989,7 @@ __device__ __forceinline__ void sd_loop(const FfnArgs &a, int row, int hh, int n
 }
 
 // FD: routed down format (q2k or q4k).
-template <int FD>
+template <int FD, bool FAST>
 __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
     const FfnArgs &a = g.a;
     __shared__ int tile_off[257];
@@ -930,7 +998,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
     __shared__ int dst[TOK];
     __shared__ float hfac[TOK];                                 // routed rows: 2^sigma of the row's token
     __shared__ uint4 tiles[2][TOK * 32];
-    __shared__ __attribute__((aligned(16))) _Float16 hsum[2][2][TOK][16];     // [tile buffer][hi, lo]
+    __shared__ __attribute__((aligned(16))) _Float16 hsum[2][TOK][16];
     Item it;
     if (!get_item(a, a.H, ROWS, a.H, tile_off, it)) return;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -959,8 +1027,11 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
         if constexpr (FD == FMT_Q4K) {
             const int nkb = I / KB;
             const int64_t NB = (int64_t)a.E * H * nkb, bl0 = ((int64_t)it.e * H + row) * nkb;
-            if (two) q4_loop<true>(a.down, NB, bl0, nkb, n, hh, src, tiles, hsum[0], dprev, mprev, acc, accm);
-            else q4_loop<false>(a.down, NB, bl0, nkb, n, hh, src, tiles, hsum[0], dprev, mprev, acc, accm);
+            if (two) q4_loop<true>(a.down, NB, bl0, nkb, n, hh, src, tiles, hsum, dprev, mprev, acc, accm);
+            else q4_loop<false>(a.down, NB, bl0, nkb, n, hh, src, tiles, hsum, dprev, mprev, acc, accm);
+        } else if constexpr (FAST) {
+            if (two) dn_loop_fast<true>(a, it.e, row, hh, n, src, tiles, acc);
+            else dn_loop_fast<false>(a, it.e, row, hh, n, src, tiles, acc);
         } else {
             if (two) dn_loop<true>(a, it.e, row, hh, n, src, tiles, hsum, dprev, mprev, acc, accm);
             else dn_loop<false>(a, it.e, row, hh, n, src, tiles, hsum, dprev, mprev, acc, accm);
@@ -973,8 +1044,13 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
                 if (d >= 0) a.slot_out[(int64_t)d * H + row] = (acc[tf][v] * dprev - accm[tf][v] * mprev) * hfac[tt];
             }
     } else {
-        if (two) sd_loop<true>(a, row, hh, n, src, src_lo, tiles, acc);
-        else sd_loop<false>(a, row, hh, n, src, src_lo, tiles, acc);
+        if constexpr (FAST) {
+            if (two) sd_loop_fast<true>(a, row, hh, n, src, tiles, acc);
+            else sd_loop_fast<false>(a, row, hh, n, src, tiles, acc);
+        } else {
+            if (two) sd_loop<true>(a, row, hh, n, src, src_lo, tiles, acc);
+            else sd_loop<false>(a, row, hh, n, src, src_lo, tiles, acc);
+        }
 #pragma unroll
         for (int tf = 0; tf < 2; ++tf)
 #pragma unroll
@@ -1073,14 +1149,19 @@ hipError_t launch_ffn_gemm(const FfnArgs &a, hipStream_t st) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int rpi = a.fmt_gu == FMT_Q4K ? ROWS / 2 : ROWS;
         const int G = max_tiles * (a.I / rpi) + (a.Is > 0 ? st_tiles * (a.Is / ROWS) : 0);
-        if (a.fmt_gu == FMT_Q4K) hipLaunchKernelGGL(k_gemm_gateup<FMT_Q4K>, dim3(G), dim3(NTHR), 0, st, g);
-        else hipLaunchKernelGGL(k_gemm_gateup<FMT_IQ2X>, dim3(G), dim3(NTHR), 0, st, g);
+        // fast mode changes the shared expert's h planes here (one bf16 plane); the routed gate/up rows stay exact
+        if (a.fmt_gu == FMT_Q4K && a.fast) hipLaunchKernelGGL((k_gemm_gateup<FMT_Q4K, true>), dim3(G), dim3(NTHR), 0, st, g);
+        else if (a.fmt_gu == FMT_Q4K) hipLaunchKernelGGL((k_gemm_gateup<FMT_Q4K, false>), dim3(G), dim3(NTHR), 0, st, g);
+        else if (a.fast) hipLaunchKernelGGL((k_gemm_gateup<FMT_IQ2X, true>), dim3(G), dim3(NTHR), 0, st, g);
+        else hipLaunchKernelGGL((k_gemm_gateup<FMT_IQ2X, false>), dim3(G), dim3(NTHR), 0, st, g);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (a.stages & STAGE_DOWN) {
         const int G = max_tiles * (a.H / ROWS) + (a.Is > 0 ? st_tiles * (a.H / ROWS) : 0);
-        if (a.fmt_d == FMT_Q4K) hipLaunchKernelGGL(k_gemm_down<FMT_Q4K>, dim3(G), dim3(NTHR), 0, st, g);
-        else hipLaunchKernelGGL(k_gemm_down<FMT_Q2K>, dim3(G), dim3(NTHR), 0, st, g);
+        if (a.fmt_d == FMT_Q4K && a.fast) hipLaunchKernelGGL((k_gemm_down<FMT_Q4K, true>), dim3(G), dim3(NTHR), 0, st, g);
+        else if (a.fmt_d == FMT_Q4K) hipLaunchKernelGGL((k_gemm_down<FMT_Q4K, false>), dim3(G), dim3(NTHR), 0, st, g);
+        else if (a.fast) hipLaunchKernelGGL((k_gemm_down<FMT_Q2K, true>), dim3(G), dim3(NTHR), 0, st, g);
+        else hipLaunchKernelGGL((k_gemm_down<FMT_Q2K, false>), dim3(G), dim3(NTHR), 0, st, g);
         e = hipGetLastError();
     }
     return e;

@@ -51,6 +51,7 @@ struct FfnArgs {
     int32_t *hsig;                     // [T] exponent of the routed fp16 h per token (workspace; fp16-h kernels)
     void *ws;
     int stages;                        // bit 0: gate/up + SwiGLU, bit 1: down
+    int fast;                          // approximate grouped-GEMM kernels (MOE_PRECISION_FAST)
     // One-token routing inside the gate/up launch (T == 1, k <= SEL_MAXK): when sel_logits is set, every routed
     // gate/up workgroup selects the token's experts from these E fp32 logits itself (topk_idx is not read), and
     // the workgroup of the first selected expert's first rows writes the routing outputs below, as moe_route does.

@@ -10,7 +10,7 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import (FMT_IQ2X, PATH_AUTO, LayerDesc, moe_combine, moe_combine_steer, moe_expert_ffn,
+from . import (FMT_IQ2X, PATH_AUTO, PRECISION_EXACT, LayerDesc, moe_combine, moe_combine_steer, moe_expert_ffn,
                moe_expert_ffn_workspace, moe_layer, moe_layer_workspace, moe_prepare_weights, moe_route,
                moe_route_workspace, moe_weight_bytes)
 
@@ -73,7 +73,7 @@ class DeviceLayer:
         del canon
         return prep
 
-    def make_desc(self, path=PATH_AUTO) -> LayerDesc:
+    def make_desc(self, path=PATH_AUTO, precision=PRECISION_EXACT) -> LayerDesc:
         d = LayerDesc()
         d.hidden, d.inter, d.n_experts, d.top_k = self.H, self.I, self.E, self.k
         d.gate_up_fmt, d.down_fmt = self.gate_up_fmt, self.down_fmt
@@ -83,6 +83,7 @@ class DeviceLayer:
         if self.shared is not None:
             d.shared_gate, d.shared_up, d.shared_down = (s.data_ptr() for s in self.shared)
         d.path = path
+        d.precision = precision
         return d
 
     def clone(self) -> "DeviceLayer":

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
     MOE_OK = 0,
@@ -79,6 +79,24 @@ typedef enum { MOE_FMT_IQ2X = 1, MOE_FMT_Q2K = 2, MOE_FMT_Q4K = 3 } moe_format;
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GENERIC = 1, MOE_PATH_GEMV = 2, MOE_PATH_GEMM = 3 } moe_path;
 
 /*
+ * Precision of the expert FFN.  EXACT (default): decoded weights are exact and
+ * every product accumulates in fp32 (the layer within 1e-3 relative L2 per
+ * token of the binary64 reference).  FAST: the opt-in approximate mode, the
+ * counterpart of the exact/approximate kernel choice the ds4-server option
+ * listing offers ("DwarfStar4 / ds4.c" user report on modu-print.com, the
+ * quality option): in the grouped-GEMM kernels (more than 8 tokens) every
+ * q2k down weight is q * fp16(d sc) - fp16(dmin m) in one fp16 fused
+ * multiply-add (no per-16 sums of h and no min products, no rescaling of the
+ * accumulators between blocks), and the shared expert's SwiGLU output is one
+ * bf16 plane instead of a hi + lo pair (half the shared down products);
+ * gate/up and q4k rows stay exact.  The layer then lies within 5e-3 relative
+ * L2 per token of the reference.  The decode and verify kernels (up to 8
+ * tokens) are bound by the weight stream, gain nothing from an approximation,
+ * and run exactly in both modes.
+ */
+typedef enum { MOE_PRECISION_EXACT = 0, MOE_PRECISION_FAST = 1 } moe_precision;
+
+/*
  * Description of one layer (host struct; read during the call only).
  *   hidden (H), inter (I), n_experts (E), top_k (k): 1 <= k <= E <= 256.
  *   gate, up: E stacked [I][H] matrices, down: E stacked [H][I] matrices, each
@@ -90,6 +108,7 @@ typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GENERIC = 1, MOE_PATH_GEMV = 2, MOE_P
  *   shared_inter (Is): 0 = no shared expert; else shared_gate, shared_up
  *     [Is][H] and shared_down [H][Is], bf16 row-major.
  *   path: kernel family for moe_expert_ffn (MOE_PATH_AUTO normally).
+ *   precision: MOE_PRECISION_EXACT (0, normally) or MOE_PRECISION_FAST.
  */
 typedef struct {
     int32_t hidden, inter, n_experts, top_k;
@@ -99,6 +118,7 @@ typedef struct {
     int32_t shared_inter;
     const void *shared_gate, *shared_up, *shared_down;
     int32_t path;
+    int32_t precision;
 } moe_layer_desc;
 
 /* MOE_ABI_VERSION of the built library. */

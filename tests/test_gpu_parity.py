@@ -805,3 +805,60 @@ def test_layer_call_graph_replay_matches_eager(m, name):
         torch.cuda.synchronize()
         assert torch.equal(bg.topk_idx, be.topk_idx)
         assert torch.equal(bg.y, be.y), f"replay {r}"
+
+
+# ----------------------------------------------------------------------------
+# the approximate fast mode (MOE_PRECISION_FAST): grouped-GEMM kernels only
+# ----------------------------------------------------------------------------
+FAST_TOL = 5e-3
+
+
+@pytest.mark.parametrize("name,T", [("small", 37), ("mid", 300), ("small_mix_a", 37), ("small_mix_b", 37),
+                                    ("prefill", 512), ("long", 2048)])
+def test_fast_mode_within_its_tolerance(m, name, T):
+    """The opt-in fast mode (q2k down weights as one fp16 fused multiply-add each, the shared expert's h in one bf16
+    plane) against the oracle at its stated 5e-3 per-token relative L2, with routing unchanged; it must differ from
+    the exact mode (it is a different computation) on the layers it applies to."""
+    from bit_quantized_moe_permute_amd import PRECISION_FAST
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward
+    note(f"fast mode {name} T={T}")
+    L = _layer("decode" if name in ("prefill", "long") else name)
+    sp = synth.SPECS[name]
+    _, bias = synth.make_router(sp)
+    x = synth.activations(name, T, sp.hidden, True)
+    DL = DeviceLayer.from_synth(L)
+    DL.bias = None if bias is None else torch.from_numpy(bias).cuda()
+    fast = DL.make_desc(precision=PRECISION_FAST)
+    b_ex, b_fa = LayerBuffers.allocate(DL, T), LayerBuffers.allocate(DL, T)
+    forward(DL, dev_x(x), b_ex)
+    forward(DL, dev_x(x), b_fa, desc=fast)
+    torch.cuda.synchronize()
+    ref = oracle.layer(x, L.w_router, sp.top_k, sp.n_experts, sp.inter, sp.gate_up_fmt, L.gate, L.up, sp.down_fmt,
+                       L.down, L.codebook, bias=bias, shared=L.shared)
+    assert torch.equal(b_fa.topk_idx, b_ex.topk_idx)
+    err = rel_l2_rows(b_fa.y.cpu().numpy(), ref["y"])
+    err_ex = rel_l2_rows(b_ex.y.cpu().numpy(), ref["y"])
+    note(f"  fast max per-token rel L2 = {err.max():.3e} (exact {err_ex.max():.3e})")
+    assert err.max() <= FAST_TOL
+    assert err_ex.max() <= TOL
+    assert not torch.equal(b_fa.y, b_ex.y)
+
+
+@pytest.mark.parametrize("name,T", [("small", 1), ("small", 3), ("small", 8), ("small_q4k", 37)])
+def test_fast_mode_is_exact_where_it_does_not_apply(m, name, T):
+    """Decode and verify calls (up to 8 tokens), and q4k routed experts with no shared expert planes of their own,
+    give the exact mode's bits in fast mode except for the shared expert's single-plane h."""
+    from bit_quantized_moe_permute_amd import PRECISION_FAST
+    from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward
+    note(f"fast mode not applied {name} T={T}")
+    L = _layer(name)
+    sp = L.spec
+    x = dev_x(synth.activations(name, T, sp.hidden, True, seed=2100 + T))
+    DL = DeviceLayer.from_synth(L)
+    b_ex, b_fa = LayerBuffers.allocate(DL, T), LayerBuffers.allocate(DL, T)
+    forward(DL, x, b_ex)
+    forward(DL, x, b_fa, desc=DL.make_desc(precision=PRECISION_FAST))
+    torch.cuda.synchronize()
+    assert torch.equal(b_fa.slot_out, b_ex.slot_out)
+    if T <= 8:
+        assert torch.equal(b_fa.y, b_ex.y)
