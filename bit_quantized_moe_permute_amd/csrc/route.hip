@@ -125,89 +125,94 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
     }
 }
 
-// Stable counting sort of the T*k slots by expert (one workgroup).  Each token
-// carries k distinct experts, so inside a tile of tokens the rank of slot
-// (t, e) among expert e's slots is the number of tile tokens before t that
-// chose e: a popcount over a per-expert token bitmap.
-constexpr int PERM_TILE = 1024;                    // tokens per tile
-constexpr int PERM_WORDS = PERM_TILE / 64;         // bitmap words per expert
+// Stable counting sort of the T*k slots by expert, one 256-thread workgroup per
+// expert.  Slots are taken in blocks of PERM_BLK: wave w of the workgroup holds
+// slots w*PERM_BLK/4 .. of a block in registers, 64 per lane (slot = block
+// start + w*PERM_BLK/4 + 64 j + lane), all requested at once.  Every workgroup
+// counts all slots per expert in LDS (the topk array is read from the cache by
+// all of them) and takes its expert's offset and active position from the
+// exclusive scans of the counts.  Then, per block, each wave counts its matches
+// by ballot, the waves' counts give each wave its first position, and the
+// matching slots are written in slot order (position = the ballot's lower-lane
+// popcount).
+constexpr int PERM_BLK = 4 * 64 * 64;              // slots per block: 4 waves x 64 lanes x 64 registers
 
-__global__ __launch_bounds__(1024) void k_permute(const int32_t *__restrict__ topk_idx, int T, int k, int E,
-                                                  int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
-                                                  int32_t *__restrict__ active) {
-    __shared__ unsigned long long bm[256 * PERM_WORDS];
-    __shared__ uint16_t wpre[256 * PERM_WORDS];
-    __shared__ int cnt[256], base[256], tilecnt[256];
-    const int tid = threadIdx.x;
-    const int64_t S = (int64_t)T * k;
-    if (tid < 256) cnt[tid] = 0;
+__global__ __launch_bounds__(256) void k_permute(const int32_t *__restrict__ topk_idx, int T, int k, int E,
+                                                 int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+                                                 int32_t *__restrict__ active) {
+    __shared__ int cnt[256];
+    __shared__ int wsum[4];
+    __shared__ int base_e, apre_e;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, e = blockIdx.x;
+    const int S = T * k, nblk = (S + PERM_BLK - 1) / PERM_BLK;
+    int v[64];
+    auto load = [&](int b0) {
+#pragma unroll
+        for (int j = 0; j < 64; ++j) {
+            const int sl = b0 + wv * (PERM_BLK / 4) + 64 * j + lane;
+            v[j] = sl < S ? topk_idx[sl] : -1;
+        }
+    };
+    cnt[tid] = 0;
     __syncthreads();
-    for (int64_t s = tid; s < S; s += blockDim.x) atomicAdd(&cnt[topk_idx[s]], 1);
+    for (int b = 0; b < nblk; ++b) {
+        load(b * PERM_BLK);
+#pragma unroll
+        for (int j = 0; j < 64; ++j)
+            if (v[j] >= 0) atomicAdd(&cnt[v[j]], 1);
+    }
     __syncthreads();
-    // exclusive scans of the counts and of the active flags (256 entries, one wave)
-    if (tid < 64) {
-        int c[4], a[4], cs = 0, as = 0;
+    if (wv == 0) {                                           // exclusive scans of the counts and active flags
+        int c[4], cs = 0, as = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            int e = 4 * tid + i;
-            c[i] = e < E ? cnt[e] : 0;
-            a[i] = c[i] > 0;
+            const int ee = 4 * lane + i;
+            c[i] = ee < E ? cnt[ee] : 0;
             cs += c[i];
-            as += a[i];
+            as += c[i] > 0;
         }
-        int ci = cs, ai = as;                       // inclusive scan over lanes
+        int ci = cs, ai = as;
         for (int o = 1; o < 64; o <<= 1) {
-            int u = __shfl_up(ci, o, 64), v = __shfl_up(ai, o, 64);
-            if (tid >= o) { ci += u; ai += v; }
+            const int u = __shfl_up(ci, o, 64), vv = __shfl_up(ai, o, 64);
+            if (lane >= o) { ci += u; ai += vv; }
         }
         int cpre = ci - cs, apre = ai - as;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            int e = 4 * tid + i;
-            if (e < E) {
-                offsets[e] = cpre;
-                base[e] = cpre;
-                if (a[i]) active[1 + apre] = e;
-            }
+            if (4 * lane + i == e) { base_e = cpre; apre_e = apre; }
             cpre += c[i];
-            apre += a[i];
+            apre += c[i] > 0;
         }
-        if (tid == 63) {
+        if (e == 0 && lane == 63) {
             offsets[E] = ci;
             active[0] = ai;
         }
     }
     __syncthreads();
-    for (int t0 = 0; t0 < T; t0 += PERM_TILE) {
-        const int nt = min(PERM_TILE, T - t0);
-        for (int i = tid; i < 256 * PERM_WORDS; i += blockDim.x) bm[i] = 0ull;
+    if (tid == 0) {
+        offsets[e] = base_e;
+        if (cnt[e] > 0) active[1 + apre_e] = e;
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int run = base_e;                                        // this expert's next position
+    for (int b = 0; b < nblk; ++b) {
+        if (nblk > 1) load(b * PERM_BLK);                    // one block: still in registers
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < 64; ++j) c += __popcll(__ballot(v[j] == e));
+        if (lane == 0) wsum[wv] = c;
         __syncthreads();
-        for (int i = tid; i < nt * k; i += blockDim.x) {
-            int tt = i / k;
-            int e = topk_idx[(int64_t)(t0 + tt) * k + (i % k)];
-            atomicOr(&bm[e * PERM_WORDS + (tt >> 6)], 1ull << (tt & 63));
+        int pos = run;
+        for (int q = 0; q < wv; ++q) pos += wsum[q];
+        run += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+#pragma unroll
+        for (int j = 0; j < 64; ++j) {
+            const bool m = v[j] == e;
+            const unsigned long long ball = __ballot(m);
+            if (m) perm[pos + __popcll(ball & below)] = b * PERM_BLK + wv * (PERM_BLK / 4) + 64 * j + lane;
+            pos += __popcll(ball);
         }
-        __syncthreads();
-        if (tid < E) {
-            int run = 0;
-            for (int wd = 0; wd < PERM_WORDS; ++wd) {
-                wpre[tid * PERM_WORDS + wd] = (uint16_t)run;
-                run += __popcll(bm[tid * PERM_WORDS + wd]);
-            }
-            tilecnt[tid] = run;
-        }
-        __syncthreads();
-        for (int i = tid; i < nt * k; i += blockDim.x) {
-            int tt = i / k;
-            int64_t s = (int64_t)(t0 + tt) * k + (i % k);
-            int e = topk_idx[s];
-            int wd = tt >> 6;
-            unsigned long long below = bm[e * PERM_WORDS + wd] & ((1ull << (tt & 63)) - 1ull);
-            perm[base[e] + wpre[e * PERM_WORDS + wd] + __popcll(below)] = (int32_t)s;
-        }
-        __syncthreads();
-        if (tid < E) base[tid] += tilecnt[tid];
-        __syncthreads();
+        __syncthreads();                                     // wsum is reused by the next block
     }
 }
 
@@ -399,7 +404,7 @@ __global__ __launch_bounds__(1024) void k_select_small(const float *__restrict__
 typedef __attribute__((ext_vector_type(16))) float rb_acc_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 rb_bf16x8_t;
 
-constexpr int RB_WAVES = 4;          // K quarters per workgroup
+constexpr int RB_WAVES = 8;          // K slices per workgroup
 
 __device__ __forceinline__ rb_acc_t rb_mfma(uint4 a, uint4 b, rb_acc_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(rb_bf16x8_t, a),
@@ -414,35 +419,27 @@ __device__ __forceinline__ bool has_subnormal(uint32_t v) {
     return (lo != 0u && lo < 0x80u) || (hi != 0u && hi < 0x80u);
 }
 
-// Workgroups 0 .. n_tiles-1: a 32-token x 32-expert tile of bounds, wave w
-// summing the K quarter w, the quarters added in order; workgroups past that:
-// one expert row each, flagged in wflag when it holds a subnormal value.
-__global__ __launch_bounds__(256) void k_router_bounds(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
-                                                       const float *__restrict__ bias, int T, int H, int E,
-                                                       float *__restrict__ lo, float *__restrict__ hi,
-                                                       int32_t *__restrict__ wflag, int n_tiles) {
+// A 32-token x 32-expert tile of bounds per workgroup, wave w summing the K slice w (of RB_WAVES), the slices added
+// in order; the workgroups of the first token tile also flag, in wflag, the expert rows that hold a subnormal value
+// (from the router rows they load anyway).
+__global__ __launch_bounds__(64 * RB_WAVES) void k_router_bounds(const uint16_t *__restrict__ x,
+                                                                 const uint16_t *__restrict__ w,
+                                                                 const float *__restrict__ bias, int T, int H, int E,
+                                                                 float *__restrict__ lo, float *__restrict__ hi,
+                                                                 int32_t *__restrict__ wflag) {
     __shared__ float red[2][RB_WAVES][16][64];
+    __shared__ int sflag[RB_WAVES][64];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if ((int)blockIdx.x >= n_tiles) {
-        const int e = blockIdx.x - n_tiles;
-        const uint4 *row = reinterpret_cast<const uint4 *>(w + (int64_t)e * H);
-        bool sub = false;
-        for (int i = tid; i < H / 8; i += blockDim.x) {
-            const uint4 v = row[i];
-            sub = sub || has_subnormal(v.x) || has_subnormal(v.y) || has_subnormal(v.z) || has_subnormal(v.w);
-        }
-        const int any = __syncthreads_or(sub ? 1 : 0);
-        if (tid == 0) wflag[e] = any;
-        return;
-    }
     const int nte = (E + 31) / 32;
     const int t0 = (blockIdx.x / nte) * 32, e0 = (blockIdx.x % nte) * 32;
+    const bool flags = t0 == 0;                                // uniform
     const int r = lane & 31, hh = lane >> 5;
     const uint16_t *xr = x + (int64_t)min(t0 + r, T - 1) * H + 32 * hh;
     const uint16_t *wr = w + (int64_t)min(e0 + r, E - 1) * H + 32 * hh;
     const int kq = H / RB_WAVES, kb = wv * kq;
     rb_acc_t acc = {}, aac = {};
     uint4 av[4], bv[4], na[4], nb[4];
+    bool sub = false;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         av[j] = *reinterpret_cast<const uint4 *>(xr + kb + 8 * j);
@@ -460,6 +457,11 @@ __global__ __launch_bounds__(256) void k_router_bounds(const uint16_t *__restric
             acc = rb_mfma(av[j], bv[j], acc);
             aac = rb_mfma(rb_abs(av[j]), rb_abs(bv[j]), aac);
         }
+        if (flags)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sub = sub || has_subnormal(bv[j].x) || has_subnormal(bv[j].y) || has_subnormal(bv[j].z) ||
+                      has_subnormal(bv[j].w);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             av[j] = na[j];
@@ -471,13 +473,19 @@ __global__ __launch_bounds__(256) void k_router_bounds(const uint16_t *__restric
         red[0][wv][v][lane] = acc[v];
         red[1][wv][v][lane] = aac[v];
     }
+    if (flags) sflag[wv][lane] = sub ? 1 : 0;
     __syncthreads();
-    // thread (wave q, lane l): outputs v = 4q .. 4q+3 of lane l's column
+    if (flags && tid < 32 && e0 + tid < E) {
+        int any = 0;
+        for (int q = 0; q < RB_WAVES; ++q) any |= sflag[q][tid] | sflag[q][tid + 32];
+        wflag[e0 + tid] = any;
+    }
+    // thread (wave q, lane l): outputs v = (16 / RB_WAVES) q + i of lane l's column
     const double nr = (double)(H + 8);
     const double eps = nr * 0x1p-23 * 1.0001;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int v = 4 * wv + i;
+    for (int i = 0; i < 16 / RB_WAVES; ++i) {
+        const int v = (16 / RB_WAVES) * wv + i;
         float a = red[0][0][v][lane], s = red[1][0][v][lane];
 #pragma unroll
         for (int q = 1; q < RB_WAVES; ++q) {
@@ -712,9 +720,9 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
         float *lo = a.bounds_ws, *hi = a.bounds_ws + (size_t)a.T * a.E;
         int32_t *wflag = reinterpret_cast<int32_t *>(hi + (size_t)a.T * a.E);
         const int n_tiles = ((a.T + 31) / 32) * ((a.E + 31) / 32);
-        hipLaunchKernelGGL(k_router_bounds, dim3(n_tiles + a.E), dim3(256), 0, st,
+        hipLaunchKernelGGL(k_router_bounds, dim3(n_tiles), dim3(64 * RB_WAVES), 0, st,
                            static_cast<const uint16_t *>(a.x), static_cast<const uint16_t *>(a.w), a.bias, a.T, a.H,
-                           a.E, lo, hi, wflag, n_tiles);
+                           a.E, lo, hi, wflag);
         if ((e = hipGetLastError()) != hipSuccess) return e;
 #define MOE_SELECT(NJ_)                                                                                     \
     case 64 * NJ_:                                                                                          \
@@ -735,7 +743,7 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
         }
 #undef MOE_SELECT
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, st, a.topk_idx, a.T, a.k, a.E, a.offsets, a.perm,
+        hipLaunchKernelGGL(k_permute, dim3(a.E), dim3(256), 0, st, a.topk_idx, a.T, a.k, a.E, a.offsets, a.perm,
                            a.active);
         return hipGetLastError();
     }
@@ -757,7 +765,7 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(k_topk, dim3((a.T + 3) / 4), dim3(256), 0, st, a.logits_ws, a.T, a.E, a.k, a.topk_idx,
                        a.topk_w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, st, a.topk_idx, a.T, a.k, a.E, a.offsets, a.perm, a.active);
+    hipLaunchKernelGGL(k_permute, dim3(a.E), dim3(256), 0, st, a.topk_idx, a.T, a.k, a.E, a.offsets, a.perm, a.active);
     return hipGetLastError();
 }
 
