@@ -33,6 +33,8 @@ from __future__ import annotations
 from dataclasses import dataclass, field
 from typing import Callable, Optional
 
+import os
+
 import numpy as np
 
 FMT_IQ2X, FMT_Q2K, FMT_Q4K, FMT_BF16 = 1, 2, 3, 4
@@ -78,14 +80,35 @@ def _clip_round(g: np.random.Generator, n: int, mean: float, std: float, lo: int
     return np.clip(np.rint(g.normal(mean, std, size=n)), lo, hi).astype(np.uint8)
 
 
+_IQ2X_ROWS = None
+
+
+def _iq2x_row_table() -> np.ndarray:
+    """65536-entry table taking a uniform 16-bit draw to a codebook row, with the row frequencies recorded in
+    tests/golden/iq2x_index_freq.txt (those of quantized N(0, 0.02) weights with the seeded codebook)."""
+    global _IQ2X_ROWS
+    if _IQ2X_ROWS is None:
+        path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "tests", "golden",
+                            "iq2x_index_freq.txt")
+        counts = np.loadtxt(path, dtype=np.int64)
+        assert counts.shape == (256,)
+        cdf = np.cumsum(counts) / counts.sum()
+        u = (np.arange(65536) + 0.5) / 65536.0
+        _IQ2X_ROWS = np.minimum(np.searchsorted(cdf, u, side="right"), 255).astype(np.uint8)
+    return _IQ2X_ROWS
+
+
 def random_blocks(fmt: int, nblocks: int, seed: int, tensor: int, part: int = 0) -> np.ndarray:
     """`nblocks` canonical blocks drawn field by field (uint8, nblocks*block_bytes)."""
     g = rng(seed, tensor, part)
     bb = BLOCK_BYTES[fmt]
     out = np.frombuffer(bytearray(g.bytes(nblocks * bb)), dtype=np.uint8).reshape(nblocks, bb)
     if fmt == FMT_IQ2X:
-        d = np.clip(g.normal(4.4e-4, 5.5e-5, size=nblocks), 3.0e-4, 7.0e-4)
+        d = np.clip(g.normal(6.56e-4, 7.9e-5, size=nblocks), 4.7e-4, 1.02e-3)
         out[:, 0:2] = _fp16_bits(d).view(np.uint8).reshape(nblocks, 2)
+        # codebook rows with the quantizer's frequencies (bytes 0..3 of each 8-byte group record)
+        rows = _iq2x_row_table()[g.integers(0, 65536, size=(nblocks, 8, 4), dtype=np.uint16)]
+        out[:, 2:].reshape(nblocks, 8, 8)[:, :, 0:4] = rows
         s = _clip_round(g, nblocks * 8, 11.5, 2.3, 0, 15).reshape(nblocks, 8)
         aux_hi = out[:, 2:].reshape(nblocks, 8, 8)[:, :, 7]          # byte holding bits 24..31 of aux
         out[:, 2:].reshape(nblocks, 8, 8)[:, :, 7] = (aux_hi & 0x0F) | (s << 4)
