@@ -23,10 +23,10 @@ PRECISION_EXACT, PRECISION_FAST = 0, 1
 ABI_VERSION = 3
 
 EXPORTS = [
-    "moe_abi_version", "moe_last_error", "moe_weight_bytes", "moe_prepare_weights", "moe_dequantize",
-    "moe_route_workspace", "moe_route", "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_expert_gate_up",
-    "moe_expert_down", "moe_combine", "moe_combine_steer", "moe_probe_stream_read", "moe_expert_ffn_noalloc",
-    "moe_layer_workspace", "moe_layer",
+    "moe_abi_version", "moe_sync_debug", "moe_last_error", "moe_weight_bytes", "moe_prepare_weights",
+    "moe_dequantize", "moe_route_workspace", "moe_route", "moe_expert_ffn_workspace", "moe_expert_ffn",
+    "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_combine_steer", "moe_probe_stream_read",
+    "moe_expert_ffn_noalloc", "moe_layer_workspace", "moe_layer",
 ]
 
 
@@ -58,6 +58,8 @@ def _load():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.moe_abi_version.restype = ctypes.c_int
     L.moe_abi_version.argtypes = []
+    L.moe_sync_debug.restype = ctypes.c_int
+    L.moe_sync_debug.argtypes = []
     L.moe_last_error.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
     L.moe_weight_bytes.restype = sz
@@ -169,6 +171,10 @@ def _dt(t) -> int:
 # ----------------------------------------------------------------------------
 def moe_abi_version() -> int:
     return lib.moe_abi_version()
+
+
+def moe_sync_debug() -> bool:
+    return bool(lib.moe_sync_debug())
 
 
 def moe_last_error() -> str:

@@ -1,11 +1,13 @@
 // C-ABI entry points of libmoe2bit: argument checking on the host, then kernel
 // dispatch on the caller's stream.  Nothing here allocates device memory or
-// synchronizes; no C++ exception crosses the interface.
+// synchronizes (unless MOE_SYNC_DEBUG asks for it); no C++ exception crosses
+// the interface.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -29,7 +31,27 @@ moe_status ok() {
     return MOE_OK;
 }
 
-moe_status from_hip(hipError_t e, const char *what) {
+// MOE_SYNC_DEBUG, read once per process: any value but "" or "0" turns it on.
+bool sync_debug() {
+    static const bool on = [] {
+        const char *v = std::getenv("MOE_SYNC_DEBUG");
+        return v && *v && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+// Result of a group of launches on stream s.  With the debug switch on, the call first waits for s (unless s is
+// being captured into a graph, where waiting is not allowed) so that a fault in those kernels is reported by the
+// entry point that launched them.
+moe_status from_hip(hipError_t e, const char *what, hipStream_t s) {
+    if (e == hipSuccess && sync_debug()) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(s, &cs);
+        if (e == hipSuccess && cs == hipStreamCaptureStatusNone) {
+            e = hipStreamSynchronize(s);
+            if (e == hipSuccess) e = hipGetLastError();
+        }
+    }
     if (e == hipSuccess) return ok();
     return fail(MOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
@@ -63,6 +85,8 @@ extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
+int moe_sync_debug(void) { return sync_debug() ? 1 : 0; }
+
 const char *moe_last_error(void) { return g_err; }
 
 size_t moe_weight_bytes(int32_t fmt, int64_t n_mats, int64_t rows, int64_t cols) {
@@ -81,7 +105,8 @@ moe_status moe_prepare_weights(int32_t fmt, int64_t n_mats, int64_t rows, int64_
     const char *c = static_cast<const char *>(canonical), *p = static_cast<const char *>(prepared);
     if (c < p + bytes && p < c + bytes) return fail(MOE_ERR_INVALID_ARG, "moe_prepare_weights: buffers overlap");
     const int64_t NB = n_mats * rows * cols / 256;
-    return from_hip(moe::launch_prepare(fmt, NB, canonical, prepared, (hipStream_t)stream), "moe_prepare_weights");
+    return from_hip(moe::launch_prepare(fmt, NB, canonical, prepared, (hipStream_t)stream), "moe_prepare_weights",
+                    (hipStream_t)stream);
 }
 
 moe_status moe_dequantize(int32_t fmt, const void *prepared, int64_t n_mats, int64_t rows, int64_t cols,
@@ -98,7 +123,7 @@ moe_status moe_dequantize(int32_t fmt, const void *prepared, int64_t n_mats, int
     const int64_t per = rows * cols / 256;
     return from_hip(moe::launch_dequant(fmt, n_mats * per, mat_begin * per, mat_count * per, prepared, codebook, out,
                                         (hipStream_t)stream),
-                    "moe_dequantize");
+                    "moe_dequantize", (hipStream_t)stream);
 }
 
 // logits [T][E] fp32 | bounds of the matrix-core router: lo, hi [T][E] fp32, expert flags [E] int32
@@ -147,7 +172,7 @@ moe_status moe_route(const void *x, int32_t x_dt, int32_t n_tokens, int32_t hidd
     moe_status st = route_args("moe_route", x, x_dt, n_tokens, hidden, w_router, w_dt, n_experts, bias, top_k,
                                topk_idx, topk_w, logits, expert_offsets, perm, active, ws, ws_bytes, a);
     if (st != MOE_OK) return st;
-    return from_hip(moe::launch_route(a, (hipStream_t)stream), "moe_route");
+    return from_hip(moe::launch_route(a, (hipStream_t)stream), "moe_route", (hipStream_t)stream);
 }
 
 static moe_status check_layer(const moe_layer_desc *L, const char *fn) {
@@ -329,7 +354,7 @@ static moe_status expert_call(const char *fn, int stages, const moe_layer_desc *
     if (path == MOE_PATH_GEMV) e = moe::launch_ffn_gemv(a, (hipStream_t)stream);
     else if (path == MOE_PATH_GEMM) e = moe::launch_ffn_gemm(a, (hipStream_t)stream);
     else e = moe::launch_ffn_generic(a, (hipStream_t)stream);
-    return from_hip(e, fn);
+    return from_hip(e, fn, (hipStream_t)stream);
 }
 
 moe_status moe_expert_ffn(const moe_layer_desc *L, const void *x, int32_t x_dt, int32_t n_tokens,
@@ -369,7 +394,7 @@ moe_status moe_combine(const float *slot_out, const float *topk_w, const float *
     if (!aligned(slot_out, 4) || !aligned(y, 4) || !aligned(topk_w, 4) || (shared_out && !aligned(shared_out, 4)))
         return fail(MOE_ERR_INVALID_ARG, "moe_combine: misaligned pointer");
     return from_hip(moe::launch_combine(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, y, (hipStream_t)stream),
-                    "moe_combine");
+                    "moe_combine", (hipStream_t)stream);
 }
 
 moe_status moe_combine_steer(const float *slot_out, const float *topk_w, const float *shared_out, int32_t n_tokens,
@@ -383,7 +408,7 @@ moe_status moe_combine_steer(const float *slot_out, const float *topk_w, const f
     if (!std::isfinite(steer_f)) return fail(MOE_ERR_INVALID_ARG, "moe_combine_steer: steering strength not finite");
     return from_hip(moe::launch_combine_steer(slot_out, topk_w, shared_out, n_tokens, top_k, hidden, steer_v, steer_f,
                                               y, (hipStream_t)stream),
-                    "moe_combine_steer");
+                    "moe_combine_steer", (hipStream_t)stream);
 }
 
 static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
@@ -419,7 +444,7 @@ moe_status moe_layer(const moe_layer_desc *L, const void *x, int32_t x_dt, int32
                            choose_path(L, probe) == MOE_PATH_GEMV && moe::ffn_gemv_supported(probe);
     const hipStream_t hs = (hipStream_t)stream;
     if (in_kernel) {
-        if ((st = from_hip(moe::launch_route_logits(ra, hs), fn)) != MOE_OK) return st;
+        if ((st = from_hip(moe::launch_route_logits(ra, hs), fn, hs)) != MOE_OK) return st;
         const InKernelRoute r{ra.logits_ws, topk_idx, topk_w, expert_offsets, perm, active};
         st = expert_call(fn, moe::STAGE_GATE_UP, L, x, x_dt, n_tokens, topk_idx, expert_offsets, perm, active,
                          nullptr, nullptr, fws, fbytes, stream, false, &r);
@@ -427,15 +452,16 @@ moe_status moe_layer(const moe_layer_desc *L, const void *x, int32_t x_dt, int32
         st = expert_call(fn, moe::STAGE_DOWN, L, x, x_dt, n_tokens, topk_idx, expert_offsets, perm, active, slot_out,
                          shared_out, fws, fbytes, stream);
     } else {
-        if ((st = from_hip(moe::launch_route(ra, hs), fn)) != MOE_OK) return st;
+        if ((st = from_hip(moe::launch_route(ra, hs), fn, hs)) != MOE_OK) return st;
         st = expert_call(fn, moe::STAGE_GATE_UP | moe::STAGE_DOWN, L, x, x_dt, n_tokens, topk_idx, expert_offsets,
                          perm, active, slot_out, shared_out, fws, fbytes, stream);
     }
     if (st != MOE_OK) return st;
     const int T = n_tokens, k = L->top_k, H = L->hidden;
     if (steer_v)
-        return from_hip(moe::launch_combine_steer(slot_out, topk_w, shared_out, T, k, H, steer_v, steer_f, y, hs), fn);
-    return from_hip(moe::launch_combine(slot_out, topk_w, shared_out, T, k, H, y, hs), fn);
+        return from_hip(moe::launch_combine_steer(slot_out, topk_w, shared_out, T, k, H, steer_v, steer_f, y, hs), fn,
+                        hs);
+    return from_hip(moe::launch_combine(slot_out, topk_w, shared_out, T, k, H, y, hs), fn, hs);
 }
 
 moe_status moe_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t n_blocks, void *stream) {
@@ -445,7 +471,7 @@ moe_status moe_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, 
     if (n_blocks < 1 || n_blocks > (1 << 20))
         return fail(MOE_ERR_INVALID_ARG, "moe_probe_stream_read: n_blocks outside [1, 2^20]");
     return from_hip(moe::launch_stream_read(buf, (int64_t)bytes, sink, n_blocks, (hipStream_t)stream),
-                    "moe_probe_stream_read");
+                    "moe_probe_stream_read", (hipStream_t)stream);
 }
 
 }  // extern "C"

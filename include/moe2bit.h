@@ -124,6 +124,16 @@ typedef struct {
 /* MOE_ABI_VERSION of the built library. */
 int moe_abi_version(void);
 
+/* 1 if the library waits for the stream after each group of launches, else 0.
+ * Set by the environment variable MOE_SYNC_DEBUG (any value but "" or "0"),
+ * read once per process at the first call.  With it on, every entry point that
+ * launches kernels synchronizes its stream before returning (not while the
+ * stream is being captured into a graph) and returns MOE_ERR_DEVICE with the
+ * device's error text if a kernel it launched failed, so that a fault is
+ * reported by the call that caused it.  A debugging aid: it serializes the
+ * host with the device. */
+int moe_sync_debug(void);
+
 /* Text for the last failure on the calling thread ("" if none). Host string,
  * owned by the library, valid until the next call on this thread. */
 const char *moe_last_error(void);
