@@ -251,6 +251,50 @@ __global__ __launch_bounds__(256) void k_router_logits_small(const void *__restr
     }
 }
 
+// bf16 x and W_r with H a multiple of 512: one wave per (expert, token), grid
+// (E, T), so that the 2 MB of a 4096 x 256 router spread over every CU.  The
+// wave reads the expert's row and the token's row with 16-byte loads (H/512
+// per lane each) and passes them through LDS, from where lane p takes
+// elements p, p+64, ... in increasing order: the same products and the same
+// sum order as k_router_logits_small, with an eighth of the load instructions.
+template <int NJ>
+__global__ __launch_bounds__(64) void k_router_logits_vec(const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ w,
+                                                          const float *__restrict__ bias, int E,
+                                                          float *__restrict__ logits,
+                                                          float *__restrict__ logits_copy) {
+    constexpr int H = 64 * NJ, NV = H / 512;
+    static_assert(NV >= 1, "H must be a multiple of 512");
+    __shared__ __attribute__((aligned(16))) uint16_t ws[H], xs[H];
+    const int lane = threadIdx.x, e = blockIdx.x, t = blockIdx.y;
+    const uint4 *wr = reinterpret_cast<const uint4 *>(w + (int64_t)e * H);
+    const uint4 *xr = reinterpret_cast<const uint4 *>(x + (int64_t)t * H);
+    uint4 wv[NV], xv[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        wv[j] = wr[64 * j + lane];
+        xv[j] = xr[64 * j + lane];
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        reinterpret_cast<uint4 *>(ws)[64 * j + lane] = wv[j];
+        reinterpret_cast<uint4 *>(xs)[64 * j + lane] = xv[j];
+    }
+    __syncthreads();
+    double v = 0.0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+        v = __fma_rn((double)bf16_bits_to_f32(ws[lane + 64 * j]), (double)bf16_bits_to_f32(xs[lane + 64 * j]), v);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v = v + __shfl_down(v, s, 64);
+    if (lane == 0) {
+        float l = (float)v;
+        if (bias) l = (float)((double)l + (double)bias[e]);
+        logits[(int64_t)t * E + e] = l;
+        if (logits_copy) logits_copy[(int64_t)t * E + e] = l;
+    }
+}
+
 // Top-k, weights and permutation for T <= 8 tokens in one workgroup of 1024
 // threads.  Expert e of token t carries the key (orderable logit bits, then
 // 255 - e): a larger key is a larger logit, ties going to the lower index, and
@@ -674,6 +718,25 @@ namespace moe {
 
 template <bool XB, bool WB>
 hipError_t launch_logits_small(const RouteArgs &a, hipStream_t st) {
+    if constexpr (XB && WB) {
+        if (a.H % 512 == 0 && (((uintptr_t)a.x | (uintptr_t)a.w) & 15u) == 0) {   // 16-byte row loads
+            const uint16_t *x = static_cast<const uint16_t *>(a.x), *w = static_cast<const uint16_t *>(a.w);
+#define MOE_LOGITS_VEC(NJ_)                                                                                  \
+    case 64 * NJ_:                                                                                           \
+        hipLaunchKernelGGL(k_router_logits_vec<NJ_>, dim3(a.E, a.T), dim3(64), 0, st, x, w, a.bias, a.E,      \
+                           a.logits_ws, a.logits_out);                                                       \
+        break;
+            switch (a.H) {
+                MOE_LOGITS_VEC(64)
+                MOE_LOGITS_VEC(32)
+                MOE_LOGITS_VEC(16)
+                MOE_LOGITS_VEC(8)
+                default: return hipErrorInvalidValue;
+            }
+#undef MOE_LOGITS_VEC
+            return hipGetLastError();
+        }
+    }
     const dim3 grd((a.E + 3) / 4, a.T);
 #define MOE_LOGITS(NJ_)                                                                                      \
     case 64 * NJ_:                                                                                           \
