@@ -774,7 +774,7 @@ hipError_t launch_route_logits(const RouteArgs &a, hipStream_t st) {
 // request for the logits themselves (those come from the full binary64 router).
 bool bounded_route(const RouteArgs &a) {
     return a.x_bf16 && a.w_bf16 && a.T > SMALL_T && a.H % 512 == 0 && a.H <= 4096 && !a.logits_out &&
-           a.bounds_ws != nullptr;
+           a.bounds_ws != nullptr && (((uintptr_t)a.x | (uintptr_t)a.w) & 15u) == 0;   // 16-byte row loads
 }
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t st) {

@@ -244,6 +244,43 @@ def test_route_many_tokens_subnormal_and_large_inputs(m):
         _check_route(m, x, w, E, k)
 
 
+@pytest.mark.parametrize("T", [1, 3, 300])
+def test_route_inputs_only_4_byte_aligned(m, T):
+    """x and the router at addresses that are 4-byte but not 16-byte aligned (views 2 bf16 values into larger
+    buffers): the routers that read rows with 16-byte loads are skipped, and the result is the same bits as from
+    aligned inputs, and the oracle's."""
+    note(f"route unaligned T={T}")
+    H, E, k = 4096, 256, 8
+    w, _ = synth.make_router("decode")
+    x = synth.activations("decode", T, H, True, seed=3300 + T)
+    bias = synth.normal_f32(5, 11, (E,), 0.5)
+
+    def unaligned(a):
+        buf = torch.empty(a.size + 8, dtype=torch.bfloat16, device="cuda")
+        v = buf[2: 2 + a.size].view(a.shape)
+        v.copy_(torch.from_numpy(a.view(np.int16)).view(torch.bfloat16))
+        assert v.data_ptr() % 16 != 0 and v.data_ptr() % 4 == 0
+        return v
+
+    i32 = dict(dtype=torch.int32, device="cuda")
+    outs = []
+    for xd, wd in ((dev_x(x), dev_x(w)), (unaligned(x), unaligned(w))):
+        idx = torch.empty(T, k, **i32)
+        tw = torch.empty(T, k, dtype=torch.float32, device="cuda")
+        off = torch.empty(E + 1, **i32)
+        perm = torch.empty(T * k, **i32)
+        act = torch.full((E + 1,), -7, **i32)
+        ws = torch.empty(max(m.moe_route_workspace(T, E, k), 256), dtype=torch.uint8, device="cuda")
+        m.moe_route(xd, wd, E, k, idx, tw, off, perm, act, ws, bias=torch.from_numpy(bias).cuda())
+        torch.cuda.synchronize()
+        outs.append((idx.cpu().numpy(), tw.cpu().numpy(), off.cpu().numpy(), perm.cpu().numpy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    _, oi, ow = oracle.route(x, w, k, bias)
+    assert np.array_equal(outs[1][0], oi)
+    assert np.abs(outs[1][1].astype(np.float64) - ow).max() <= 1e-6
+
+
 def test_route_summation_order_golden(m):
     """tests/golden/router_order.txt: cancellation cases where the fixed order decides the logit."""
     from test_oracle_layer import _router_order_cases
