@@ -723,31 +723,33 @@ __device__ __forceinline__ void dn_load(const FfnArgs &a, int e, int row, int kb
     w.dm = f16_bits_to_f32(dd >> 16);
 }
 
-// per-16 sums of the h tile (fp16 hi + lo), 512 threads = 64 rows x 8 pairs of sub-blocks
-__device__ __forceinline__ void tile_sums(const uint4 *tile, _Float16 (*hs)[TOK][16]) {
-    const int m = threadIdx.x >> 3, qd = threadIdx.x & 7;
+// x_store for an h tile, plus its per-16 sums: the two threads that hold a 16-wide sub-block (chunks 2 sb and
+// 2 sb + 1 of a row) add their halves in fp32 and store the sum as fp16 hi (hs[m][sb]) + lo (hs[m][16 + sb]).
+// The barrier that publishes the tile publishes the sums.
+template <int NV>
+__device__ __forceinline__ void x_store_sums16(const XStageN<NV> &xs, uint4 *tile, _Float16 (*hs)[32]) {
 #pragma unroll
-    for (int sbq = 0; sbq < 2; ++sbq) {
-        const int sb = 2 * qd + sbq;
-        float s = 0.f;
+    for (int i = 0; i < NV; ++i) {
+        const int idx = threadIdx.x + NTHR * i, m = idx >> 5, c = idx & 31;
+        tile[tpos(m, c)] = xs.v[i];
+        const uint32_t wds[4] = {xs.v[i].x, xs.v[i].y, xs.v[i].z, xs.v[i].w};
+        float sm = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-            const uint4 u = tile[tpos(m, 2 * sb + cc)];
-            const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f16x2_t pr = __builtin_bit_cast(f16x2_t, wds[i]);
-                s += (float)pr.x + (float)pr.y;
-            }
+        for (int k = 0; k < 4; ++k) {
+            const f16x2_t pr = __builtin_bit_cast(f16x2_t, wds[k]);
+            sm += (float)pr.x + (float)pr.y;
         }
-        const _Float16 shi = (_Float16)s;
-        hs[0][m][sb] = shi;
-        hs[1][m][sb] = (_Float16)(s - (float)shi);
+        sm += __shfl_xor(sm, 1, 64);
+        if ((c & 1) == 0) {
+            const _Float16 hi = (_Float16)sm;
+            hs[m][c >> 1] = hi;
+            hs[m][16 + (c >> 1)] = (_Float16)(sm - (float)hi);
+        }
     }
 }
 
 template <bool two>
-__device__ __forceinline__ void dn_block(const DnW &w, const uint4 *tile, _Float16 (*hs)[TOK][16], int n, int hh,
+__device__ __forceinline__ void dn_block(const DnW &w, const uint4 *tile, const _Float16 (*hs)[32], int n, int hh,
                                          float &dprev, float &mprev, f32x16_t (&acc)[2], f32x16_t (&accm)[2]) {
     const float s1 = rescale(w.d, dprev), s2 = rescale(w.dm, mprev);
     scale_acc(acc[0], s1);
@@ -779,17 +781,17 @@ __device__ __forceinline__ void dn_block(const DnW &w, const uint4 *tile, _Float
         if constexpr (two) acc[1] = mfma_f16(frag16(tile, 32 + n, c), b, acc[1]);
     }
     // min term: K = the 16 sub-blocks; A = per-16 sums (hi, lo), B = mins
-    accm[0] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[0][n][8 * hh]), mins, accm[0]);
-    accm[0] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[1][n][8 * hh]), mins, accm[0]);
+    accm[0] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[n][8 * hh]), mins, accm[0]);
+    accm[0] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[n][16 + 8 * hh]), mins, accm[0]);
     if constexpr (two) {
-        accm[1] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[0][32 + n][8 * hh]), mins, accm[1]);
-        accm[1] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[1][32 + n][8 * hh]), mins, accm[1]);
+        accm[1] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[32 + n][8 * hh]), mins, accm[1]);
+        accm[1] = mfma_f16(*reinterpret_cast<const f16x8_t *>(&hs[32 + n][16 + 8 * hh]), mins, accm[1]);
     }
 }
 
 template <bool two>
 __device__ __forceinline__ void dn_loop(const FfnArgs &a, int e, int row, int hh, int n, const uint16_t *const *src,
-                                        uint4 (*tiles)[TOK * 32], _Float16 (*hsum)[TOK][16], float &dprev,
+                                        uint4 (*tiles)[TOK * 32], _Float16 (*hsum)[TOK][32], float &dprev,
                                         float &mprev, f32x16_t (&acc)[2], f32x16_t (&accm)[2]) {
     const int I = a.I, H = a.H, nkb = I / KB;
     const int64_t nb_row = I / KB, nb_mat = (int64_t)H * nb_row, NB = nb_mat * a.E;
@@ -797,28 +799,24 @@ __device__ __forceinline__ void dn_loop(const FfnArgs &a, int e, int row, int hh
     XStageN<two ? 4 : 2> xs;                             // a one-fragment tile needs its first 32 rows only
     x_fetch(src, 0, xs);
     dn_load(a, e, row, 0, hh, nb_row, nb_mat, NB, w0);
-    x_store(xs, tiles[0]);
+    x_store_sums16(xs, tiles[0], hsum[0]);
     __syncthreads();
     for (int kb = 0; kb < nkb; kb += 2) {
         const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
-        tile_sums(tiles[0], hsum);
-        __syncthreads();
         x_fetch(src, k1 * KB, xs);
         dn_load(a, e, row, k1, hh, nb_row, nb_mat, NB, w1);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
-        dn_block<two>(w0, tiles[0], hsum, n, hh, dprev, mprev, acc, accm);
+        dn_block<two>(w0, tiles[0], hsum[0], n, hh, dprev, mprev, acc, accm);
         __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
-        x_store(xs, tiles[1]);
+        x_store_sums16(xs, tiles[1], hsum[1]);
         __syncthreads();
         if (kb + 1 >= nkb) break;
-        tile_sums(tiles[1], hsum);
-        __syncthreads();
         x_fetch(src, k2 * KB, xs);
         dn_load(a, e, row, k2, hh, nb_row, nb_mat, NB, w0);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch above the compute
-        dn_block<two>(w1, tiles[1], hsum, n, hh, dprev, mprev, acc, accm);
+        dn_block<two>(w1, tiles[1], hsum[1], n, hh, dprev, mprev, acc, accm);
         __builtin_amdgcn_sched_barrier(0);     // store the next tile after the compute
-        x_store(xs, tiles[0]);
+        x_store_sums16(xs, tiles[0], hsum[0]);
         __syncthreads();
     }
 }
@@ -998,7 +996,9 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
     __shared__ int dst[TOK];
     __shared__ float hfac[TOK];                                 // routed rows: 2^sigma of the row's token
     __shared__ uint4 tiles[2][TOK * 32];
-    __shared__ __attribute__((aligned(16))) _Float16 hsum[2][TOK][16];
+    __shared__ __attribute__((aligned(16))) _Float16 hsum_lds[2 * TOK * 32];   // two buffers of per-row sums
+    _Float16 (*hsum)[TOK][16] = reinterpret_cast<_Float16 (*)[TOK][16]>(hsum_lds);      // q4k: per 32
+    _Float16 (*hsum16)[TOK][32] = reinterpret_cast<_Float16 (*)[TOK][32]>(hsum_lds);    // q2k: per 16
     Item it;
     if (!get_item(a, a.H, ROWS, a.H, tile_off, it)) return;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -1033,8 +1033,8 @@ __global__ __launch_bounds__(NTHR) void k_gemm_down(GemmArgs g) {
             if (two) dn_loop_fast<true>(a, it.e, row, hh, n, src, tiles, acc);
             else dn_loop_fast<false>(a, it.e, row, hh, n, src, tiles, acc);
         } else {
-            if (two) dn_loop<true>(a, it.e, row, hh, n, src, tiles, hsum, dprev, mprev, acc, accm);
-            else dn_loop<false>(a, it.e, row, hh, n, src, tiles, hsum, dprev, mprev, acc, accm);
+            if (two) dn_loop<true>(a, it.e, row, hh, n, src, tiles, hsum16, dprev, mprev, acc, accm);
+            else dn_loop<false>(a, it.e, row, hh, n, src, tiles, hsum16, dprev, mprev, acc, accm);
         }
 #pragma unroll
         for (int tf = 0; tf < 2; ++tf)
