@@ -34,7 +34,8 @@
  *    unimplemented combination returns MOE_ERR_UNSUPPORTED; a HIP launch error
  *    returns MOE_ERR_DEVICE.  moe_last_error() describes the last failure on
  *    the calling thread.  Faults inside kernels surface at the caller's next
- *    synchronization.  No C++ exception crosses this interface.
+ *    synchronization (at the faulting call itself when MOE_SYNC_DEBUG is set,
+ *    see moe_sync_debug).  No C++ exception crosses this interface.
  *  - Non-finite inputs are outside the contract.
  *
  * Canonical block formats (256 weights per block; blocks run along the
