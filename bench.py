@@ -355,6 +355,25 @@ def main():
     no_cycling = {"tokens_per_s": round(K / nwall, 1), "ms_per_step": round(nwall * 1e3 / K, 5), "layer_copies": 1}
     log(f"decode on one layer copy (no cycling): {K / nwall:.0f} tokens/s")
 
+    # per-call latency: eager moe_layer calls enqueued back to back (no host sync in between), a HIP event pair on
+    # the launch stream around each; the spread of single-token GPU times, graph launch not involved
+    n_lat = min(K, 1000)
+    cs = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_lat)]
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    for i in range(n_lat):
+        evs[i][0].record(cs)
+        step(i)
+        evs[i][1].record(cs)
+    torch.cuda.synchronize()
+    lat = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    latency = {"calls": n_lat, "p50_us": round(lat[n_lat // 2], 2),
+               "p99_us": round(lat[min(n_lat - 1, (99 * n_lat) // 100)], 2), "max_us": round(lat[-1], 2),
+               "method": "HIP event pair on the launch stream around each eager one-token moe_layer call"}
+    log(f"decode per-call latency (eager): p50 {latency['p50_us']} us, p99 {latency['p99_us']} us")
+
     # speculative-verify micro-batch: 3 independent tokens per step
     vK = args.verify_steps
     vx_np = synth.activations("verify", 3 * vK, H, True)
@@ -522,6 +541,7 @@ def main():
         "verify": verify,
         "decode_steer": steer,
         "decode_no_cycling": no_cycling,
+        "decode_latency": latency,
         "decode_q4k": decode_q4k,
         "prefill": prefill,
     }
