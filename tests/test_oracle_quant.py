@@ -72,17 +72,23 @@ def test_iq2x_index_is_bruteforce_argmin():
 
 
 def test_iq2x_scale_rule():
-    """d = fp16(max|w| / 93); group scale s = clamp(round((max_g|w|/(3d) - 1)/2), 0, 15)."""
+    """The block scale d is the fp16 value nearest max|w| / 93 (no neighbouring fp16 value is closer), and each
+    group's scale s is, by search over all sixteen values, the one whose largest magnitude 3(2s+1)d lies closest to
+    the group's largest |w|."""
     cb = synth.codebook()
     w = _w(64, 3).astype(np.float64)
     b = oracle.quantize(oracle.FMT_IQ2X, w.astype(np.float32), cb).reshape(-1, 66)
-    d = b[:, 0:2].copy().view(np.float16).astype(np.float64)[:, 0]
-    want_d = (np.abs(w.reshape(-1, 256)).max(-1) / 3 / 31).astype(np.float16).astype(np.float64)
-    assert np.array_equal(d, want_d)
+    d16 = b[:, 0:2].copy().view(np.float16)[:, 0]
+    d = d16.astype(np.float64)
+    target = np.abs(w.reshape(-1, 256)).max(-1) / 93
+    for di, ti in zip(d16, target):
+        up, down = np.nextafter(di, np.float16(np.inf)), np.nextafter(di, np.float16(0))
+        assert abs(float(di) - ti) <= abs(float(up) - ti) and abs(float(di) - ti) <= abs(float(down) - ti)
     aux = b[:, 2:].reshape(-1, 8, 8)[:, :, 4:].copy().view(np.uint32)[..., 0]
-    G = np.abs(w.reshape(-1, 8, 32)).max(-1) / 3
-    want_s = np.clip(np.rint((G / d[:, None] - 1) / 2), 0, 15)
-    assert np.array_equal((aux >> 28).astype(np.float64), want_s)
+    G = np.abs(w.reshape(-1, 8, 32)).max(-1)
+    cand = 3.0 * (2 * np.arange(16) + 1)[None, None, :] * d[:, None, None]   # [block][group][s]
+    want_s = np.abs(cand - G[..., None]).argmin(-1)
+    assert np.array_equal((aux >> 28).astype(np.int64), want_s)
 
 
 def test_iq2x_parity_and_sign_choice():
