@@ -760,8 +760,10 @@ LAYER_CALL_CASES = [
     # one token: routing selected inside the gate/up launch (MFMA iq2x kernel; VALU q4k kernel; top-16)
     ("small", 1, False), ("decode", 1, False), ("decode", 1, True), ("small_q4k", 1, False),
     ("small_mix_a", 1, False), ("small_mix_b", 1, False), ("mid_k16", 1, False), ("mid", 1, True),
-    # several tokens: the three calls inside one
-    ("small", 3, False), ("small", 37, True), ("mid", 70, False), ("tiny", 4, False),
+    # several tokens: the three calls inside one (2..8 tokens on the verify kernels, with one wave per workgroup
+    # at hidden 512 and eight at 4096, top-16 with 64 slots, a bias, steering; then the grouped GEMM)
+    ("small", 3, False), ("small", 8, True), ("decode", 2, False), ("decode", 3, True), ("decode", 8, False),
+    ("mid", 5, False), ("mid_k16", 4, False), ("small", 37, True), ("mid", 70, False), ("tiny", 4, False),
 ]
 
 
@@ -812,18 +814,19 @@ def test_layer_call_matches_the_three_calls(m, name, T, steer):
     assert err.max() <= TOL
 
 
-@pytest.mark.parametrize("name", ["mid", "decode"])
-def test_layer_call_graph_replay_matches_eager(m, name):
-    """moe_layer at one token captured once in a HIP graph: every replay on new inputs equals an eager call."""
+@pytest.mark.parametrize("name,T", [("mid", 1), ("decode", 1), ("decode", 3), ("small", 5)])
+def test_layer_call_graph_replay_matches_eager(m, name, T):
+    """moe_layer at one token (selection in the decode gate/up launch) or a few (the verify kernels) captured once
+    in a HIP graph: every replay on new inputs equals an eager call."""
     from bit_quantized_moe_permute_amd.layer import DeviceLayer, LayerBuffers, forward_layer
-    note(f"layer call graph replay {name}")
+    note(f"layer call graph replay {name} T={T}")
     L = _layer(name)
     sp = L.spec
     DL = DeviceLayer.from_synth(L)
-    xs = [dev_x(synth.activations(name, 1, sp.hidden, sp.x_bf16, seed=1800 + r)) for r in range(3)]
+    xs = [dev_x(synth.activations(name, T, sp.hidden, sp.x_bf16, seed=1800 + r)) for r in range(3)]
     xin = torch.empty_like(xs[0])
     xin.copy_(xs[0])
-    bg, be = LayerBuffers.allocate(DL, 1), LayerBuffers.allocate(DL, 1)
+    bg, be = LayerBuffers.allocate(DL, T), LayerBuffers.allocate(DL, T)
     forward_layer(DL, xin, bg)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
