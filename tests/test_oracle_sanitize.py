@@ -17,14 +17,14 @@ import pytest
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-DRIVER = os.path.join(HERE, "oracle_sanitize_main.c")
+MAIN_C = os.path.join(HERE, "oracle_sanitize_main.c")
 ORACLE = os.path.join(ROOT, "oracle", "moe_oracle.c")
 BASE_FLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math"]
 SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 
 def _build(out, extra):
-    subprocess.check_call(["gcc", *BASE_FLAGS, *extra, "-o", out, DRIVER, ORACLE, "-lm"])
+    subprocess.check_call(["gcc", *BASE_FLAGS, *extra, "-o", out, MAIN_C, ORACLE, "-lm"])
 
 
 def _run(exe, env_extra):
